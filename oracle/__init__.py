@@ -1,0 +1,240 @@
+"""fp64 CPU oracle for exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or calls it, and the oracle shares
+no code with it.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, OpenMP over rows); this
+module builds it with gcc and marshals numpy arrays through ctypes.  Inputs
+are raw 16-bit bit patterns (``numpy.uint16``) in [B,H,N,d] order, so the
+oracle sees exactly the bits the GPU sees.
+
+Pages cited (by tag and section):
+  [P-notes] "FlashAttention v1 & v2 笔记" (yiran529.github.io)
+  [P-baidu] "FlashAttention 优化原理与实现要点解析" (cloud.baidu.com)
+  [P-wmrh]  "FlashAttention V2 核心原理与架构设计" (wmrh.cn)
+
+Functions and what pins them (tests/test_oracle.py):
+  attn_fwd        plain definition, [P-baidu] §1, §2, §4.1 -- brute force vs a
+                  library softmax, invariants, closed forms
+  attn_fwd_rows   the same on selected rows -- agreement with attn_fwd
+  attn_probs      P = Softmax(S) -- rows sum to 1, brute force
+  attn_fwd_tiled  block algorithm of [P-baidu] §4.2-§6 -- agreement with
+                  attn_fwd at several tile sizes
+  softmax_1d / softmax_online_1d  [P-baidu] §4.1 / [P-wmrh] §2.1 -- library
+                  softmax and each other
+  decode          binary16 / bfloat16 decoders -- all 65536 patterns vs a
+                  library cast, hand-checked values
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_DIR = Path(__file__).resolve().parent
+_SRC = _DIR / "oracle.c"
+_LIB = _DIR / "liboracle.so"
+
+DTYPE_F16 = 0
+DTYPE_BF16 = 1
+
+_default = None
+
+
+def build(force: bool = True, src: Path = _SRC, out: Path = _LIB) -> Path:
+    """Compile oracle.c into a shared library with gcc (fp64, no fast-math)."""
+    if not force and out.exists():
+        return out
+    tmp = out.with_suffix(".so.tmp")
+    cmd = [
+        "gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+        "-std=c11", "-Wall", "-shared", "-fPIC", str(src), "-o", str(tmp), "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _bind(lib):
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    i32 = ctypes.c_int
+    f64 = ctypes.c_double
+    lib.oracle_decode.argtypes = [p, i32, i64, p]
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_softmax_1d.argtypes = [p, i64, p]
+    lib.oracle_softmax_online_1d.argtypes = [p, i64, p]
+    lib.oracle_attn_fwd.argtypes = [p, p, p, i32, i64, i64, i64, i64, i32, f64, p, p]
+    lib.oracle_attn_fwd_rows.argtypes = [p, p, p, i32, i64, i64, i64, i64, i32, f64,
+                                         p, i64, p, p]
+    lib.oracle_attn_probs.argtypes = [p, p, p, i32, i64, i64, i64, i64, i32, f64, p]
+    lib.oracle_attn_fwd_tiled.argtypes = [p, p, p, i32, i64, i64, i64, i64, i32, f64,
+                                          i64, i64, p, p]
+    for name in ("oracle_decode", "oracle_num_threads", "oracle_attn_fwd",
+                 "oracle_attn_fwd_rows", "oracle_attn_probs", "oracle_attn_fwd_tiled"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.oracle_softmax_1d.restype = None
+    lib.oracle_softmax_online_1d.restype = None
+    return lib
+
+
+def _load():
+    global _default
+    if _default is None:
+        if not _LIB.exists():
+            build()
+        _default = Oracle(_LIB)
+    return _default._lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _bits(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint16:
+        raise TypeError("oracle inputs are raw 16-bit patterns (numpy.uint16)")
+    return x
+
+
+def _dtype_code(dtype) -> int:
+    if dtype in (DTYPE_F16, "f16", "fp16", "float16"):
+        return DTYPE_F16
+    if dtype in (DTYPE_BF16, "bf16", "bfloat16"):
+        return DTYPE_BF16
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise RuntimeError(f"{what} failed with code {rc}")
+
+
+def _impl_num_threads(lib) -> int:
+    return int(lib.oracle_num_threads())
+
+
+def _impl_decode(lib, bits: np.ndarray, dtype) -> np.ndarray:
+    bits = _bits(bits)
+    out = np.empty(bits.shape, dtype=np.float64)
+    _check(lib.oracle_decode(_ptr(bits), _dtype_code(dtype), bits.size, _ptr(out)),
+           "oracle_decode")
+    return out
+
+
+def _impl_softmax_1d(lib, x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    lib.oracle_softmax_1d(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def _impl_softmax_online_1d(lib, x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    lib.oracle_softmax_online_1d(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def _shape(q, k, v):
+    if q.ndim != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B,H,N,d] shape")
+    return q.shape
+
+
+def _impl_attn_fwd(lib, q, k, v, dtype, causal: bool, scale: float):
+    """Exact attention in fp64.  Returns (o [B,H,N,d], lse [B,H,N])."""
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    B, H, N, d = _shape(q, k, v)
+    o = np.empty((B, H, N, d), dtype=np.float64)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    _check(lib.oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(dtype),
+                               B, H, N, d, int(bool(causal)), float(scale),
+                               _ptr(o), _ptr(lse)), "oracle_attn_fwd")
+    return o, lse
+
+
+def _impl_attn_fwd_rows(lib, q, k, v, dtype, causal: bool, scale: float, rows):
+    """Exact attention on selected flat rows (b*H+h)*N+i.
+    Returns (o [n_rows,d], lse [n_rows])."""
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    B, H, N, d = _shape(q, k, v)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    o = np.empty((rows.size, d), dtype=np.float64)
+    lse = np.empty((rows.size,), dtype=np.float64)
+    _check(lib.oracle_attn_fwd_rows(_ptr(q), _ptr(k), _ptr(v), _dtype_code(dtype),
+                                    B, H, N, d, int(bool(causal)), float(scale),
+                                    _ptr(rows), rows.size, _ptr(o), _ptr(lse)),
+           "oracle_attn_fwd_rows")
+    return o, lse
+
+
+def _impl_attn_probs(lib, q, k, v, dtype, causal: bool, scale: float):
+    """The attention weights P [B,H,N,N] (masked entries 0).  Tiny inputs."""
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    B, H, N, d = _shape(q, k, v)
+    p = np.empty((B, H, N, N), dtype=np.float64)
+    _check(lib.oracle_attn_probs(_ptr(q), _ptr(k), _ptr(v), _dtype_code(dtype),
+                                 B, H, N, d, int(bool(causal)), float(scale), _ptr(p)),
+           "oracle_attn_probs")
+    return p
+
+
+def _impl_attn_fwd_tiled(lib, q, k, v, dtype, causal: bool, scale: float,
+                         Br: int, Bc: int):
+    """The block algorithm (online-softmax merge) in fp64."""
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    B, H, N, d = _shape(q, k, v)
+    o = np.empty((B, H, N, d), dtype=np.float64)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    _check(lib.oracle_attn_fwd_tiled(_ptr(q), _ptr(k), _ptr(v), _dtype_code(dtype),
+                                     B, H, N, d, int(bool(causal)), float(scale),
+                                     int(Br), int(Bc), _ptr(o), _ptr(lse)),
+           "oracle_attn_fwd_tiled")
+    return o, lse
+
+
+_API = ("num_threads", "decode", "softmax_1d", "softmax_online_1d", "attn_fwd",
+        "attn_fwd_rows", "attn_probs", "attn_fwd_tiled")
+
+
+class Oracle:
+    """One loaded build of oracle.c, with the functions of this module as
+    methods.  The module-level functions use the default build; tests that
+    plant mistakes load a mutated copy through this class."""
+
+    def __init__(self, path):
+        self._lib = _bind(ctypes.CDLL(str(path)))
+
+    def __getattr__(self, name):
+        if name not in _API:
+            raise AttributeError(name)
+        fn = globals()["_impl_" + name]
+        return lambda *a, **kw: fn(self._lib, *a, **kw)
+
+
+def _module_fn(name):
+    impl = globals()["_impl_" + name]
+
+    def fn(*a, **kw):
+        return impl(_load(), *a, **kw)
+
+    fn.__name__ = name
+    fn.__doc__ = impl.__doc__
+    return fn
+
+
+num_threads = _module_fn("num_threads")
+decode = _module_fn("decode")
+softmax_1d = _module_fn("softmax_1d")
+softmax_online_1d = _module_fn("softmax_online_1d")
+attn_fwd = _module_fn("attn_fwd")
+attn_fwd_rows = _module_fn("attn_fwd_rows")
+attn_probs = _module_fn("attn_probs")
+attn_fwd_tiled = _module_fn("attn_fwd_tiled")

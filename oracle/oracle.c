@@ -1,0 +1,403 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference for exact attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark do.  It shares no code, header, table or helper with
+ * the HIP library: it has its own 16-bit decoders and its own loops.
+ *
+ * Sources (web pages; cited by tag and section):
+ *   [P-notes] "FlashAttention v1 & v2 笔记"              (yiran529.github.io)
+ *   [P-baidu] "FlashAttention 优化原理与实现要点解析"      (cloud.baidu.com)
+ *   [P-wmrh]  "FlashAttention V2 核心原理与架构设计"       (wmrh.cn)
+ *
+ * What is computed (per batch b, head h, query row i):
+ *   A_i   = {0..N-1}, or {0..i} when causal (key j <= query i);
+ *   s_j   = scale * sum_c q[i][c] * k[j][c]                  for j in A_i
+ *   o[i]  = sum_j softmax(s)_j * v[j]
+ *   lse_i = ln sum_{j in A_i} exp(s_j)
+ * i.e. Attention(Q,K,V) = Softmax(Q K^T * scale) V, [P-baidu] §1 (the formula)
+ * and §2 (S = QK^T, P = Softmax(S), O = PV).  The softmax is the max-shifted
+ * form of [P-baidu] §4.1 (max pass, then exp-sum, then normalise).  The
+ * logsumexp output packs the row maximum m and denominator l that the kernel
+ * signature in [P-wmrh] §2.3 returns separately: lse = m + ln l.
+ *
+ * Tensors are [B,H,N,d] contiguous, element (b,h,n,c) at ((b*H+h)*N+n)*d+c.
+ * Inputs are raw IEEE binary16 (dtype 0) or bfloat16 (dtype 1) bit patterns.
+ *
+ * The tiled function oracle_attn_fwd_tiled() follows the block algorithm of
+ * [P-baidu] §4.2, §4.3, §5 and §6 step by step in fp64; it exists so that the
+ * merge algebra can be checked against the plain definition.
+ *
+ * Parity pins (all in the CPU test suite): brute force against a library
+ * softmax on tiny inputs, rows of P summing to 1, constant-V, identical-K,
+ * Q = 0, causal row 0, shift and permutation invariance, the tiled merge at
+ * several tile sizes, peaky inputs, and exhaustive decoder checks.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_DTYPE_F16 0
+#define ORACLE_DTYPE_BF16 1
+
+/* ---- 16-bit decoders ---------------------------------------------------- */
+
+/* IEEE 754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits.
+ * Subnormals (exponent 0) are fraction * 2^-24. */
+static double decode_f16(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -24);
+    else if (e == 31)
+        mag = (f == 0) ? INFINITY : NAN;
+    else
+        mag = ldexp((double)(1024 + f), e - 25);
+    return sign ? -mag : mag;
+}
+
+/* bfloat16: 1 sign, 8 exponent (bias 127), 7 fraction bits.
+ * Subnormals (exponent 0) are fraction * 2^-133. */
+static double decode_bf16(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 7) & 0xff;
+    int f = h & 0x7f;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -133);
+    else if (e == 255)
+        mag = (f == 0) ? INFINITY : NAN;
+    else
+        mag = ldexp((double)(128 + f), e - 134);
+    return sign ? -mag : mag;
+}
+
+static int decode_all(const uint16_t *bits, int dtype, int64_t n, double *out)
+{
+    if (dtype == ORACLE_DTYPE_F16) {
+        for (int64_t i = 0; i < n; ++i) out[i] = decode_f16(bits[i]);
+    } else if (dtype == ORACLE_DTYPE_BF16) {
+        for (int64_t i = 0; i < n; ++i) out[i] = decode_bf16(bits[i]);
+    } else {
+        return -1;
+    }
+    return 0;
+}
+
+int oracle_decode(const uint16_t *bits, int dtype, int64_t n, double *out)
+{
+    return decode_all(bits, dtype, n, out);
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ---- 1-D softmax, two ways --------------------------------------------- */
+
+/* [P-baidu] §4.1: pass 1 finds the maximum m, pass 2 sums exp(x_j - m),
+ * pass 3 normalises each element. */
+void oracle_softmax_1d(const double *x, int64_t n, double *out)
+{
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j)
+        if (x[j] > m) m = x[j];
+    double l = 0.0;
+    for (int64_t j = 0; j < n; ++j) l += exp(x[j] - m);
+    for (int64_t j = 0; j < n; ++j) out[j] = exp(x[j] - m) / l;
+}
+
+/* [P-wmrh] §2.1: one pass keeping a running maximum m and a running sum l;
+ * each new element first rescales l by exp(m - m_new), then adds
+ * exp(x_i - m_new).  Result exp(x - m) / l.  (The page's code lost its '='
+ * and '+' signs in extraction; this is the recurrence it describes.) */
+void oracle_softmax_online_1d(const double *x, int64_t n, double *out)
+{
+    double m = -INFINITY, l = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double m_new = x[i] > m ? x[i] : m;
+        /* Boundary cases (§2.1 asks for them to be handled): while every
+         * element so far is -inf, m = -inf and l = 0; a -inf element adds
+         * weight 0 (exp(-inf - (-inf)) would be NaN). */
+        double scale_old = (m == -INFINITY) ? 0.0 : exp(m - m_new);
+        double term = (x[i] == -INFINITY) ? 0.0 : exp(x[i] - m_new);
+        l = l * scale_old + term;
+        m = m_new;
+    }
+    for (int64_t j = 0; j < n; ++j) out[j] = exp(x[j] - m) / l;
+}
+
+/* ---- exact attention, plain definition ---------------------------------- */
+
+typedef struct {
+    double *q, *k, *v;          /* decoded [B,H,N,d] */
+    int64_t B, H, N, d;
+    int causal;
+    double scale;
+} problem;
+
+static int load_problem(problem *p, const uint16_t *q, const uint16_t *k,
+                        const uint16_t *v, int dtype, int64_t B, int64_t H,
+                        int64_t N, int64_t d, int causal, double scale)
+{
+    if (B < 0 || H < 0 || N < 0 || d < 1) return -1;
+    if (dtype != ORACLE_DTYPE_F16 && dtype != ORACLE_DTYPE_BF16) return -1;
+    int64_t n = B * H * N * d;
+    p->B = B; p->H = H; p->N = N; p->d = d; p->causal = causal; p->scale = scale;
+    size_t bytes = (size_t)(n > 0 ? n : 1) * sizeof(double);
+    p->q = (double *)malloc(bytes);
+    p->k = (double *)malloc(bytes);
+    p->v = (double *)malloc(bytes);
+    if (!p->q || !p->k || !p->v) {
+        free(p->q); free(p->k); free(p->v);
+        return -2;
+    }
+    decode_all(q, dtype, n, p->q);
+    decode_all(k, dtype, n, p->k);
+    decode_all(v, dtype, n, p->v);
+    return 0;
+}
+
+static void free_problem(problem *p)
+{
+    free(p->q); free(p->k); free(p->v);
+}
+
+/* One query row.  `row` is the flat index (b*H+h)*N+i.  `s` is scratch of
+ * N doubles.  Writes d values to o_out and one to lse_out. */
+static void attn_row(const problem *p, int64_t row, double *s, double *o_out,
+                     double *lse_out)
+{
+    const int64_t N = p->N, d = p->d;
+    const int64_t bh = row / N, i = row % N;
+    const double *qi = p->q + row * d;
+    const double *kh = p->k + bh * N * d;
+    const double *vh = p->v + bh * N * d;
+    const int64_t nkeys = p->causal ? i + 1 : N;     /* |A_i| */
+
+    /* pass 1: scores and their maximum */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
+        s[j] = p->scale * dot;
+        if (s[j] > m) m = s[j];
+    }
+    /* pass 2: weights, denominator, weighted sum of V */
+    double l = 0.0;
+    for (int64_t c = 0; c < d; ++c) o_out[c] = 0.0;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        double w = exp(s[j] - m);
+        l += w;
+        for (int64_t c = 0; c < d; ++c) o_out[c] += w * vh[j * d + c];
+    }
+    /* normalise */
+    for (int64_t c = 0; c < d; ++c) o_out[c] /= l;
+    *lse_out = m + log(l);
+}
+
+/* Full forward: o is [B,H,N,d] fp64, lse is [B,H,N] fp64. */
+int oracle_attn_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    int dtype, int64_t B, int64_t H, int64_t N, int64_t d,
+                    int causal, double scale, double *o, double *lse)
+{
+    problem p;
+    int rc = load_problem(&p, q, k, v, dtype, B, H, N, d, causal, scale);
+    if (rc) return rc;
+    const int64_t rows = B * H * N;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < rows; ++r)
+                attn_row(&p, r, s, o + r * d, lse + r);
+        }
+        free(s);
+    }
+    free_problem(&p);
+    return fail ? -2 : 0;
+}
+
+/* Selected rows only: rows[t] is a flat row index (b*H+h)*N+i; outputs are
+ * packed, o_rows is [n_rows, d] and lse_rows is [n_rows]. */
+int oracle_attn_fwd_rows(const uint16_t *q, const uint16_t *k,
+                         const uint16_t *v, int dtype, int64_t B, int64_t H,
+                         int64_t N, int64_t d, int causal, double scale,
+                         const int64_t *rows, int64_t n_rows, double *o_rows,
+                         double *lse_rows)
+{
+    const int64_t total = B * H * N;
+    for (int64_t t = 0; t < n_rows; ++t)
+        if (rows[t] < 0 || rows[t] >= total) return -1;
+    problem p;
+    int rc = load_problem(&p, q, k, v, dtype, B, H, N, d, causal, scale);
+    if (rc) return rc;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t t = 0; t < n_rows; ++t)
+                attn_row(&p, rows[t], s, o_rows + t * d, lse_rows + t);
+        }
+        free(s);
+    }
+    free_problem(&p);
+    return fail ? -2 : 0;
+}
+
+/* The attention weights P = Softmax(S) themselves, [B,H,N,N] fp64, masked
+ * entries 0.  For tiny inputs only ([P-baidu] §2 step 2). */
+int oracle_attn_probs(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      int dtype, int64_t B, int64_t H, int64_t N, int64_t d,
+                      int causal, double scale, double *probs)
+{
+    problem p;
+    int rc = load_problem(&p, q, k, v, dtype, B, H, N, d, causal, scale);
+    if (rc) return rc;
+    double *s = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    if (!s) { free_problem(&p); return -2; }
+    for (int64_t r = 0; r < B * H * N; ++r) {
+        const int64_t bh = r / N, i = r % N;
+        const int64_t nkeys = causal ? i + 1 : N;
+        double *prow = probs + r * N;
+        for (int64_t j = 0; j < N; ++j) prow[j] = 0.0;
+        for (int64_t j = 0; j < nkeys; ++j) {
+            double dot = 0.0;
+            for (int64_t c = 0; c < d; ++c)
+                dot += p.q[r * d + c] * p.k[(bh * N + j) * d + c];
+            s[j] = scale * dot;
+        }
+        oracle_softmax_1d(s, nkeys, prow);
+    }
+    free(s);
+    free_problem(&p);
+    return 0;
+}
+
+/* ---- the block algorithm, in fp64 ---------------------------------------
+ *
+ * [P-baidu] §5: Q is split into blocks of Br rows (outer loop) and K/V into
+ * blocks of Bc rows (inner loop).  For each (Q block, K/V block):
+ *   1. the score block S_blk = Q_blk K_blk^T * scale;
+ *   2. per row, the block's local maximum m_new and local exponent sum
+ *      l_new = sum exp(s - m_new), and (§6) the block's local numerator
+ *      u_new = sum exp(s - m_new) v  -- numerator and denominator kept apart;
+ *   3. the running maximum m = max(m_old, m_new) and (§4.2)
+ *      l = l_old * exp(m_old - m) + l_new * exp(m_new - m);
+ *   4. (§4.3) the running output O = O_old * exp(m_old - m)
+ *      + u_new * exp(m_new - m), i.e. P_new V_new with P_new = exp(S - m);
+ *   5. repeat over the K/V blocks;
+ *   6. O_final = O / l  (§4.3, §6: one division at the end).
+ * Rows whose allowed keys miss a block entirely (causal) skip that block;
+ * [P-baidu] §7 notes whole blocks past the diagonal need no work.
+ * Br = Bc = 1 reduces to the per-element recurrence of [P-wmrh] §2.1.
+ */
+int oracle_attn_fwd_tiled(const uint16_t *q, const uint16_t *k,
+                          const uint16_t *v, int dtype, int64_t B, int64_t H,
+                          int64_t N, int64_t d, int causal, double scale,
+                          int64_t Br, int64_t Bc, double *o, double *lse)
+{
+    if (Br < 1 || Bc < 1) return -1;
+    problem p;
+    int rc = load_problem(&p, q, k, v, dtype, B, H, N, d, causal, scale);
+    if (rc) return rc;
+    double *m = (double *)malloc((size_t)Br * sizeof(double));
+    double *l = (double *)malloc((size_t)Br * sizeof(double));
+    double *acc = (double *)malloc((size_t)(Br * d) * sizeof(double));
+    double *sblk = (double *)malloc((size_t)(Br * Bc) * sizeof(double));
+    double *unew = (double *)malloc((size_t)d * sizeof(double));
+    if (!m || !l || !acc || !sblk || !unew) {
+        free(m); free(l); free(acc); free(sblk); free(unew);
+        free_problem(&p);
+        return -2;
+    }
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        const double *qh = p.q + bh * N * d;
+        const double *kh = p.k + bh * N * d;
+        const double *vh = p.v + bh * N * d;
+        for (int64_t i0 = 0; i0 < N; i0 += Br) {           /* Q blocks: outer */
+            const int64_t br = (N - i0 < Br) ? N - i0 : Br;
+            for (int64_t r = 0; r < br; ++r) {
+                m[r] = -INFINITY;
+                l[r] = 0.0;
+                for (int64_t c = 0; c < d; ++c) acc[r * d + c] = 0.0;
+            }
+            for (int64_t j0 = 0; j0 < N; j0 += Bc) {       /* K/V blocks: inner */
+                const int64_t bc = (N - j0 < Bc) ? N - j0 : Bc;
+                /* step 1: score block, masked entries -inf */
+                for (int64_t r = 0; r < br; ++r)
+                    for (int64_t t = 0; t < bc; ++t) {
+                        const int64_t i = i0 + r, j = j0 + t;
+                        if (causal && j > i) {
+                            sblk[r * Bc + t] = -INFINITY;
+                            continue;
+                        }
+                        double dot = 0.0;
+                        for (int64_t c = 0; c < d; ++c)
+                            dot += qh[i * d + c] * kh[j * d + c];
+                        sblk[r * Bc + t] = scale * dot;
+                    }
+                for (int64_t r = 0; r < br; ++r) {
+                    const double *srow = sblk + r * Bc;
+                    /* step 2: local maximum, local denominator and numerator */
+                    double m_new = -INFINITY;
+                    for (int64_t t = 0; t < bc; ++t)
+                        if (srow[t] > m_new) m_new = srow[t];
+                    if (m_new == -INFINITY) continue;   /* no allowed key here */
+                    double l_new = 0.0;
+                    for (int64_t c = 0; c < d; ++c) unew[c] = 0.0;
+                    for (int64_t t = 0; t < bc; ++t) {
+                        double w = exp(srow[t] - m_new);   /* 0 for masked */
+                        l_new += w;
+                        for (int64_t c = 0; c < d; ++c)
+                            unew[c] += w * vh[(j0 + t) * d + c];
+                    }
+                    /* step 3: merge the statistics */
+                    const double m_old = m[r];
+                    const double mm = m_old > m_new ? m_old : m_new;
+                    const double f_old = (m_old == -INFINITY) ? 0.0 : exp(m_old - mm);
+                    const double f_new = exp(m_new - mm);
+                    l[r] = l[r] * f_old + l_new * f_new;
+                    /* step 4: rescale the old numerator, add the new one */
+                    for (int64_t c = 0; c < d; ++c)
+                        acc[r * d + c] = acc[r * d + c] * f_old + unew[c] * f_new;
+                    m[r] = mm;
+                }
+            }
+            /* step 6: one division per row at the end */
+            for (int64_t r = 0; r < br; ++r) {
+                const int64_t row = bh * N + i0 + r;
+                for (int64_t c = 0; c < d; ++c)
+                    o[row * d + c] = acc[r * d + c] / l[r];
+                lse[row] = m[r] + log(l[r]);
+            }
+        }
+    }
+    free(m); free(l); free(acc); free(sblk); free(unew);
+    free_problem(&p);
+    return 0;
+}

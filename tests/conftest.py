@@ -1,0 +1,22 @@
+import os
+import sys
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+
+def pytest_configure(config):
+    config.addinivalue_line(
+        "markers", "gpu: needs an MI355X (gfx950) GPU; runs the HIP library")
+
+
+@pytest.fixture(scope="session")
+def oracle_mod():
+    import oracle
+    if not (ROOT / "oracle" / "liboracle.so").exists():
+        oracle.build()
+    return oracle

@@ -1,0 +1,199 @@
+"""Pins for the fp64 oracle, runnable against any build of oracle.c.
+
+Each pin checks the oracle against something other than itself: a library
+softmax/logsumexp on decoded inputs (torch fp64, decoding by torch's own
+cast), pure-Python loops with math.fsum, closed forms, or invariants of the
+definition.  ``run_pins(orc)`` returns the names of the pins that fail, so a
+mutated oracle (a planted mistake) can be shown to fail at least one.
+
+Pages: [P-baidu] "FlashAttention 优化原理与实现要点解析" (cloud.baidu.com),
+[P-wmrh] "FlashAttention V2 核心原理与架构设计" (wmrh.cn).
+"""
+from __future__ import annotations
+
+import json
+import math
+from pathlib import Path
+
+import numpy as np
+import torch
+
+from io_aware_transformer_amd.inputs import bits, make_qkv
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+_TD = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def to_tensor(x: np.ndarray, dtype: str) -> torch.Tensor:
+    """Values -> 16-bit torch tensor (round to nearest even)."""
+    return torch.from_numpy(np.asarray(x, dtype=np.float64)).to(_TD[dtype])
+
+
+def torch_reference(q, k, v, causal: bool, scale: float):
+    """Softmax(Q K^T * scale) V and logsumexp via torch fp64 library calls,
+    on inputs decoded by torch's own cast."""
+    q64, k64, v64 = q.double(), k.double(), v.double()
+    s = torch.matmul(q64, k64.transpose(-1, -2).contiguous()) * float(scale)
+    N = q.shape[-2]
+    if causal:
+        mask = torch.ones(N, N, dtype=torch.bool).triu(1)
+        s = s.masked_fill(mask, float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    o = torch.matmul(p, v64)
+    lse = torch.logsumexp(s, dim=-1)
+    return o.numpy(), lse.numpy(), p.numpy()
+
+
+def python_reference(q, k, v, causal: bool, scale: float):
+    """Pure-Python loops, math.fsum sums; tiny inputs only."""
+    qa, ka, va = q.double().tolist(), k.double().tolist(), v.double().tolist()
+    B, H, N, d = q.shape
+    o = np.zeros((B, H, N, d))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                keys = range(i + 1) if causal else range(N)
+                s = [scale * math.fsum(qa[b][h][i][c] * ka[b][h][j][c] for c in range(d))
+                     for j in keys]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                den = math.fsum(w)
+                for c in range(d):
+                    o[b, h, i, c] = math.fsum(w[t] * va[b][h][j][c]
+                                              for t, j in enumerate(keys)) / den
+                lse[b, h, i] = mx + math.log(den)
+    return o, lse
+
+
+def _close(a, b, tol) -> bool:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.shape != b.shape:
+        return False
+    if not (np.isfinite(a).all() and np.isfinite(b).all()):
+        return False
+    return bool(np.max(np.abs(a - b), initial=0.0) <= tol)
+
+
+def _qkv(B, H, N, d, dtype, seed, gain=1.0):
+    q, k, v = make_qkv(B, H, N, d, dtype, seed=seed, qk_gain=gain)
+    return q, k, v
+
+
+def pin_brute_force(orc) -> bool:
+    ok = True
+    for dtype in ("f16", "bf16"):
+        for causal in (False, True):
+            q, k, v = _qkv(1, 2, 17, 8, dtype, seed=3)
+            scale = float(np.float32(1 / math.sqrt(8)))
+            o, lse = orc.attn_fwd(bits(q), bits(k), bits(v), dtype, causal, scale)
+            ro, rl, _ = torch_reference(q, k, v, causal, scale)
+            ok &= _close(o, ro, 1e-12) and _close(lse, rl, 1e-12)
+    return ok
+
+
+def pin_python_loops(orc) -> bool:
+    q, k, v = _qkv(1, 1, 5, 3, "f16", seed=11)
+    ok = True
+    for causal in (False, True):
+        o, lse = orc.attn_fwd(bits(q), bits(k), bits(v), "f16", causal, 0.7)
+        po, pl = python_reference(q, k, v, causal, 0.7)
+        ok &= _close(o, po, 1e-13) and _close(lse, pl, 1e-13)
+    return ok
+
+
+def pin_tiled(orc) -> bool:
+    q, k, v = _qkv(1, 2, 23, 4, "bf16", seed=5)
+    ok = True
+    for causal in (False, True):
+        ro, rl, _ = torch_reference(q, k, v, causal, 0.5)
+        for br, bc in ((1, 1), (7, 5), (23, 23)):
+            o, lse = orc.attn_fwd_tiled(bits(q), bits(k), bits(v), "bf16", causal, 0.5, br, bc)
+            ok &= _close(o, ro, 1e-12) and _close(lse, rl, 1e-12)
+    return ok
+
+
+def pin_decode_golden(orc) -> bool:
+    g = json.loads((GOLDEN / "decode_values.json").read_text())
+    ok = True
+    for dtype in ("f16", "bf16"):
+        hx = np.array([int(h, 16) for h, _, _ in g[dtype]], dtype=np.uint16)
+        want = [float(v) for _, v, _ in g[dtype]]
+        got = orc.decode(hx, dtype)
+        for a, b in zip(got, want):
+            if math.isnan(b):
+                ok &= math.isnan(a)
+            else:
+                ok &= (a == b) and (math.copysign(1, a) == math.copysign(1, b))
+    return ok
+
+
+def pin_softmax_1d(orc) -> bool:
+    x = np.array([0.3, -2.0, 5.5, 5.5, -40.0, 1e-3, 700.0, 699.0])
+    ref = torch.softmax(torch.from_numpy(x), 0).numpy()
+    return (_close(orc.softmax_1d(x), ref, 1e-15)
+            and _close(orc.softmax_online_1d(x), ref, 1e-15))
+
+
+def pin_peaky_finite(orc) -> bool:
+    q, k, v = _qkv(1, 1, 64, 64, "f16", seed=2, gain=30.0)
+    o, lse = orc.attn_fwd(bits(q), bits(k), bits(v), "f16", False, 0.125)
+    return bool(np.isfinite(o).all() and np.isfinite(lse).all())
+
+
+def pin_causal_row0(orc) -> bool:
+    q, k, v = _qkv(2, 2, 9, 16, "bf16", seed=4)
+    o, lse = orc.attn_fwd(bits(q), bits(k), bits(v), "bf16", True, 0.25)
+    ok = np.array_equal(o[:, :, 0, :], v[:, :, 0, :].double().numpy())
+    s00 = 0.25 * (q[:, :, 0, :].double() * k[:, :, 0, :].double()).sum(-1).numpy()
+    return bool(ok and _close(lse[:, :, 0], s00, 1e-14))
+
+
+def pin_probs(orc) -> bool:
+    q, k, v = _qkv(1, 2, 12, 8, "f16", seed=6)
+    ok = True
+    for causal in (False, True):
+        p = orc.attn_probs(bits(q), bits(k), bits(v), "f16", causal, 0.4)
+        _, _, rp = torch_reference(q, k, v, causal, 0.4)
+        ok &= _close(p.sum(-1), np.ones(p.shape[:-1]), 1e-14) and _close(p, rp, 1e-14)
+    return ok
+
+
+def pin_rows(orc) -> bool:
+    q, k, v = _qkv(2, 3, 19, 8, "bf16", seed=8)
+    rows = np.array([0, 5, 18, 19, 57, 113], dtype=np.int64)
+    ok = True
+    for causal in (False, True):
+        o, lse = orc.attn_fwd_rows(bits(q), bits(k), bits(v), "bf16", causal, 0.3, rows)
+        ro, rl, _ = torch_reference(q, k, v, causal, 0.3)
+        ok &= _close(o, ro.reshape(-1, 8)[rows], 1e-12)
+        ok &= _close(lse, rl.reshape(-1)[rows], 1e-12)
+    return ok
+
+
+PINS = {
+    "brute_force": pin_brute_force,
+    "python_loops": pin_python_loops,
+    "tiled": pin_tiled,
+    "decode_golden": pin_decode_golden,
+    "softmax_1d": pin_softmax_1d,
+    "peaky_finite": pin_peaky_finite,
+    "causal_row0": pin_causal_row0,
+    "probs": pin_probs,
+    "rows": pin_rows,
+}
+
+
+def run_pins(orc) -> list:
+    """Names of the pins that fail (an exception counts as a failure)."""
+    failed = []
+    for name, fn in PINS.items():
+        try:
+            ok = fn(orc)
+        except Exception:  # a mutant may crash a pin; that is a failure
+            ok = False
+        if not ok:
+            failed.append(name)
+    return failed

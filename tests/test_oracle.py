@@ -1,0 +1,331 @@
+"""CPU pins of the fp64 oracle (no GPU).
+
+The oracle computes Softmax(Q K^T * scale) V and lse = ln sum exp(scale q.k)
+("FlashAttention 优化原理与实现要点解析" §1-§2, §4.1); the block variant follows
+the merge of §4.2-§6 of the same page.  Every test here checks it against
+something independent: torch fp64 library routines on torch-decoded inputs,
+pure-Python math.fsum loops, closed forms, or invariants of the definition.
+"""
+from __future__ import annotations
+
+import math
+import re
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+from io_aware_transformer_amd.inputs import bits, make_qkv, WORKLOADS
+from tests.oracle_pins import (PINS, python_reference, run_pins, to_tensor,
+                               torch_reference)
+
+
+# ---------------------------------------------------------------- decoders
+
+@pytest.mark.parametrize("dtype,tdt", [("f16", torch.float16), ("bf16", torch.bfloat16)])
+def test_decode_all_patterns(oracle_mod, dtype, tdt):
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle_mod.decode(allbits, dtype)
+    want = torch.from_numpy(allbits.view(np.int16)).view(tdt).double().numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_decode_golden(oracle_mod):
+    assert PINS["decode_golden"](oracle_mod)
+
+
+# ---------------------------------------------------------------- 1-D softmax
+
+def test_softmax_1d_library(oracle_mod):
+    rng = np.random.default_rng(0)
+    for n in (1, 2, 3, 10, 1000):
+        for spread in (1.0, 50.0, 800.0):
+            x = rng.standard_normal(n) * spread
+            ref = torch.softmax(torch.from_numpy(x), 0).numpy()
+            np.testing.assert_allclose(oracle_mod.softmax_1d(x), ref, rtol=1e-13, atol=1e-300)
+            np.testing.assert_allclose(oracle_mod.softmax_online_1d(x), ref, rtol=1e-12,
+                                       atol=1e-300)
+
+
+def test_softmax_1d_closed_forms(oracle_mod):
+    # two entries differing by ln 3 -> weights 1/4, 3/4
+    x = np.array([0.0, math.log(3.0)])
+    for f in (oracle_mod.softmax_1d, oracle_mod.softmax_online_1d):
+        np.testing.assert_allclose(f(x), [0.25, 0.75], rtol=1e-15)
+        np.testing.assert_allclose(f(np.full(7, 2.5)), np.full(7, 1 / 7), rtol=1e-15)
+        # -inf entries get weight 0
+        y = f(np.array([-np.inf, 1.0, -np.inf, 1.0]))
+        np.testing.assert_array_equal(y, [0.0, 0.5, 0.0, 0.5])
+
+
+# ---------------------------------------------------------------- brute force
+
+@pytest.mark.parametrize("N", [1, 2, 3, 5, 17, 64])
+@pytest.mark.parametrize("d", [1, 2, 8, 64])
+@pytest.mark.parametrize("causal", [False, True])
+def test_brute_force_library(oracle_mod, N, d, causal):
+    for dtype in ("f16", "bf16"):
+        q, k, v = make_qkv(2, 3, N, d, dtype, seed=N * 100 + d)
+        scale = float(np.float32(1 / math.sqrt(d)))
+        o, lse = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), dtype, causal, scale)
+        ro, rl, _ = torch_reference(q, k, v, causal, scale)
+        np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("scale", [0.0, -0.6, 0.125, 2.0])
+def test_python_loops(oracle_mod, causal, scale):
+    q, k, v = make_qkv(1, 2, 5, 4, "bf16", seed=21)
+    o, lse = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), "bf16", causal, scale)
+    po, pl = python_reference(q, k, v, causal, scale)
+    np.testing.assert_allclose(o, po, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, pl, rtol=0, atol=1e-13)
+
+
+def test_two_key_logistic_closed_form(oracle_mod):
+    """N=2, d=1: o_i = v0 * sigmoid(s0 - s1) + v1 * sigmoid(s1 - s0) and
+    lse_i = max(s) + log1p(exp(-|s0 - s1|))."""
+    qv = np.array([1.5, -0.75])
+    kv = np.array([2.0, 0.5])
+    vv = np.array([3.0, -1.25])
+    q = to_tensor(qv.reshape(1, 1, 2, 1), "f16")
+    k = to_tensor(kv.reshape(1, 1, 2, 1), "f16")
+    v = to_tensor(vv.reshape(1, 1, 2, 1), "f16")
+    scale = 0.8125
+    o, lse = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), "f16", False, scale)
+    sig = lambda x: 1.0 / (1.0 + math.exp(-x))
+    for i in range(2):
+        s0, s1 = scale * qv[i] * kv[0], scale * qv[i] * kv[1]
+        want_o = vv[0] * sig(s0 - s1) + vv[1] * sig(s1 - s0)
+        want_l = max(s0, s1) + math.log1p(math.exp(-abs(s0 - s1)))
+        assert o[0, 0, i, 0] == pytest.approx(want_o, abs=1e-15)
+        assert lse[0, 0, i] == pytest.approx(want_l, abs=1e-15)
+
+
+# ---------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probs_rows_sum_to_one(oracle_mod, causal):
+    q, k, v = make_qkv(2, 2, 33, 16, "f16", seed=7)
+    p = oracle_mod.attn_probs(bits(q), bits(k), bits(v), "f16", causal, 0.25)
+    np.testing.assert_allclose(p.sum(-1), 1.0, rtol=0, atol=1e-14)
+    if causal:
+        assert np.all(np.triu(np.ones((33, 33)), 1)[None, None] * p == 0)
+    # the same weights applied to V give the forward output
+    o, _ = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), "f16", causal, 0.25)
+    np.testing.assert_allclose(p @ v.double().numpy(), o, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_constant_v_rows(oracle_mod, causal):
+    q, k, _ = make_qkv(1, 3, 70, 32, "bf16", seed=9, qk_gain=2.0)
+    u = to_tensor(np.random.default_rng(1).standard_normal(32), "bf16")
+    v = u.reshape(1, 1, 1, 32).expand(1, 3, 70, 32).contiguous()
+    o, _ = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), "bf16", causal, 0.3)
+    np.testing.assert_allclose(o, np.broadcast_to(u.double().numpy(), o.shape),
+                               rtol=1e-14, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_k_rows(oracle_mod, causal):
+    B, H, N, d = 1, 2, 41, 16
+    q, _, v = make_qkv(B, H, N, d, "f16", seed=10)
+    kappa = to_tensor(np.random.default_rng(2).standard_normal((1, H, 1, d)), "f16")
+    k = kappa.expand(B, H, N, d).contiguous()
+    scale = 0.25
+    o, lse = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), "f16", causal, scale)
+    v64 = v.double().numpy()
+    counts = np.arange(1, N + 1) if causal else np.full(N, N)
+    if causal:
+        mean = np.cumsum(v64, axis=2) / counts[None, None, :, None]
+    else:
+        mean = np.broadcast_to(v64.mean(axis=2, keepdims=True), v64.shape)
+    np.testing.assert_allclose(o, mean, rtol=0, atol=1e-12)
+    qk = (q.double().numpy() * kappa.double().numpy()).sum(-1)
+    np.testing.assert_allclose(lse, scale * qk + np.log(counts)[None, None, :], rtol=0,
+                               atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_q_zero(oracle_mod, causal):
+    B, H, N, d = 2, 1, 50, 8
+    _, k, v = make_qkv(B, H, N, d, "bf16", seed=12)
+    q = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
+    o, lse = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), "bf16", causal, 0.35)
+    counts = np.arange(1, N + 1) if causal else np.full(N, N)
+    v64 = v.double().numpy()
+    mean = (np.cumsum(v64, axis=2) / counts[None, None, :, None]) if causal else \
+        np.broadcast_to(v64.mean(axis=2, keepdims=True), v64.shape)
+    np.testing.assert_allclose(o, mean, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, np.broadcast_to(np.log(counts), lse.shape), rtol=0,
+                               atol=1e-13)
+
+
+def test_causal_row0(oracle_mod):
+    assert PINS["causal_row0"](oracle_mod)
+    q, k, v = make_qkv(1, 4, 300, 64, "f16", seed=13)
+    o, lse = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), "f16", True, 0.125)
+    assert np.array_equal(o[:, :, 0, :], v[:, :, 0, :].double().numpy())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_shift_invariance(oracle_mod, causal):
+    """K' = K + 1 c^T: O unchanged, lse' = lse + scale * q.c.  Values on a
+    1/8 grid so K + c is exact in fp16."""
+    rng = np.random.default_rng(3)
+    B, H, N, d = 1, 2, 37, 8
+    kv = rng.integers(-16, 17, size=(B, H, N, d)) / 8.0
+    cv = rng.integers(-16, 17, size=(1, H, 1, d)) / 8.0
+    q, _, v = make_qkv(B, H, N, d, "f16", seed=14)
+    k = to_tensor(kv, "f16")
+    k2 = to_tensor(kv + cv, "f16")
+    assert np.array_equal(k2.double().numpy(), kv + cv)   # exact
+    o, lse = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), "f16", causal, 0.3)
+    o2, lse2 = oracle_mod.attn_fwd(bits(q), bits(k2), bits(v), "f16", causal, 0.3)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-12)
+    qc = (q.double().numpy() * cv).sum(-1)
+    np.testing.assert_allclose(lse2, lse + 0.3 * qc, rtol=0, atol=1e-12)
+
+
+def test_permutation(oracle_mod):
+    B, H, N, d = 1, 2, 29, 16
+    q, k, v = make_qkv(B, H, N, d, "bf16", seed=15)
+    o, lse = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), "bf16", False, 0.25)
+    perm = torch.from_numpy(np.random.default_rng(4).permutation(N))
+    # permuting K and V rows together leaves outputs unchanged
+    o2, lse2 = oracle_mod.attn_fwd(bits(q), bits(k[:, :, perm]), bits(v[:, :, perm]),
+                                   "bf16", False, 0.25)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-13)
+    # permuting Q rows permutes the output rows, exactly
+    o3, lse3 = oracle_mod.attn_fwd(bits(q[:, :, perm]), bits(k), bits(v), "bf16", False,
+                                   0.25)
+    assert np.array_equal(o3, o[:, :, perm.numpy()])
+    assert np.array_equal(lse3, lse[:, :, perm.numpy()])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_peaky_one_hot_limit(oracle_mod, dtype):
+    """Q, K x 30: the max-shifted softmax stays finite ("FlashAttention V2
+    核心原理与架构设计" §2.1, §4.2) and rows with a large score gap give the
+    value row of the arg-max key."""
+    B, H, N, d = 1, 2, 96, 64
+    q, k, v = make_qkv(B, H, N, d, dtype, seed=16, qk_gain=30.0)
+    scale = 0.125
+    o, lse = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), dtype, False, scale)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    s = scale * (q.double() @ k.double().transpose(-1, -2)).numpy()
+    top2 = np.sort(s, axis=-1)[..., -2:]
+    gap = top2[..., 1] - top2[..., 0]
+    arg = s.argmax(-1)
+    v64 = v.double().numpy()
+    sel = gap > 40.0
+    assert sel.sum() > 10
+    onehot = np.take_along_axis(v64, arg[..., None], axis=2)
+    np.testing.assert_allclose(o[sel], onehot[sel], rtol=0, atol=1e-6)
+    np.testing.assert_allclose(lse[sel], s.max(-1)[sel], rtol=0, atol=1e-6)
+
+
+# ---------------------------------------------------------------- block merge
+
+@pytest.mark.parametrize("N", [1, 37, 130])
+@pytest.mark.parametrize("tiles", [(1, 1), (7, 7), (64, 64), (16, 7), (5, 64), ("N", "N")])
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiled_merge_matches_plain(oracle_mod, N, tiles, causal):
+    br, bc = (N if t == "N" else t for t in tiles)
+    q, k, v = make_qkv(1, 2, N, 16, "bf16", seed=17, qk_gain=2.0)
+    o, lse = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), "bf16", causal, 0.25)
+    ot, lt = oracle_mod.attn_fwd_tiled(bits(q), bits(k), bits(v), "bf16", causal, 0.25, br, bc)
+    np.testing.assert_allclose(ot, o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lt, lse, rtol=0, atol=1e-12)
+
+
+def test_rows_subset_matches_full(oracle_mod):
+    B, H, N, d = 2, 2, 77, 32
+    for causal in (False, True):
+        q, k, v = make_qkv(B, H, N, d, "f16", seed=18)
+        o, lse = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), "f16", causal, 0.2)
+        rows = np.array([0, 1, 76, 77, 150, 307], dtype=np.int64)
+        orr, lr = oracle_mod.attn_fwd_rows(bits(q), bits(k), bits(v), "f16", causal, 0.2, rows)
+        assert np.array_equal(orr, o.reshape(-1, d)[rows])
+        assert np.array_equal(lr, lse.reshape(-1)[rows])
+    with pytest.raises(RuntimeError):
+        oracle_mod.attn_fwd_rows(bits(q), bits(k), bits(v), "f16", False, 0.2,
+                                 np.array([B * H * N], dtype=np.int64))
+
+
+def test_bad_dtype(oracle_mod):
+    with pytest.raises(ValueError):
+        oracle_mod.attn_fwd(np.zeros((1, 1, 1, 1), np.uint16), np.zeros((1, 1, 1, 1), np.uint16),
+                            np.zeros((1, 1, 1, 1), np.uint16), "f32", False, 1.0)
+
+
+def test_all_pins_pass_on_the_oracle(oracle_mod):
+    assert run_pins(oracle_mod) == []
+
+
+def test_tiny_workload_against_library(oracle_mod):
+    """The smallest forward-pass workload (B1 H2 N256 d64 fp16) in full."""
+    w = WORKLOADS["tiny"]
+    q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=0)
+    o, lse = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), w.dtype, w.causal, w.scale)
+    ro, rl, _ = torch_reference(q, k, v, w.causal, w.scale)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+# Each entry plants one plausible mistake in a copy of oracle.c; the pins
+# above must catch every one.  (old text, new text, what the mistake is)
+MUTANTS = [
+    ("s[j] = p->scale * dot;", "s[j] = dot;", "dropped scale"),
+    ("double w = exp(s[j] - m);", "double w = exp(m - s[j]);", "sign of the exponent"),
+    ("p->causal ? i + 1 : N;", "p->causal ? i : N;", "causal off by one"),
+    ("p->causal ? i + 1 : N;", "p->causal ? N : N;", "causal mask dropped"),
+    ("for (int64_t c = 0; c < d; ++c) o_out[c] /= l;", "", "normalisation dropped"),
+    ("*lse_out = m + log(l);", "*lse_out = log(l);", "lse without the max"),
+    ("o_out[c] += w * vh[j * d + c];", "o_out[c] += w * vh[i * d + c];", "V row index"),
+    ("dot += qi[c] * kh[j * d + c];", "dot += qi[c] * kh[j * d + (d - 1 - c)];",
+     "feature index of K reversed"),
+    ("if (s[j] > m) m = s[j];", "m = 0.0;", "no max subtraction"),
+    ("ldexp((double)(1024 + f), e - 25)", "ldexp((double)(1024 + f), e - 24)",
+     "binary16 exponent bias"),
+    ("mag = ldexp((double)f, -24);", "mag = ldexp((double)f, -25);", "binary16 subnormal"),
+    ("ldexp((double)(128 + f), e - 134)", "ldexp((double)(128 + f), e - 133)",
+     "bfloat16 exponent bias"),
+    ("l[r] = l[r] * f_old + l_new * f_new;", "l[r] = l[r] + l_new;",
+     "merge: denominator not rescaled"),
+    ("acc[r * d + c] = acc[r * d + c] * f_old + unew[c] * f_new;",
+     "acc[r * d + c] = acc[r * d + c] + unew[c] * f_new;", "merge: numerator not rescaled"),
+    ("const double f_new = exp(m_new - mm);", "const double f_new = exp(mm - m_new);",
+     "merge: sign of the new-block factor"),
+    ("l = l * scale_old + term;", "l = l + term;",
+     "online 1-D: sum not rescaled"),
+    ("for (int64_t j = 0; j < n; ++j) l += exp(x[j] - m);",
+     "for (int64_t j = 1; j < n; ++j) l += exp(x[j] - m);", "1-D: first term dropped"),
+]
+
+
+@pytest.fixture(scope="module")
+def oracle_source():
+    from tests.conftest import ROOT
+    return (ROOT / "oracle" / "oracle.c").read_text()
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+@pytest.mark.parametrize("old,new,what", MUTANTS, ids=[m[2] for m in MUTANTS])
+def test_planted_mistake_is_caught(oracle_source, tmp_path, old, new, what):
+    import oracle
+    assert oracle_source.count(old) == 1, f"mutation site for '{what}' not unique"
+    src = tmp_path / "mutant.c"
+    src.write_text(oracle_source.replace(old, new))
+    lib = oracle.build(src=src, out=tmp_path / "libmutant.so")
+    failed = run_pins(oracle.Oracle(lib))
+    assert failed, f"planted mistake '{what}' passed every pin"
