@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Forward-pass throughput of the MI355X exact-attention kernel.
+
+One step = one fa_fwd call over the whole batch of the workload (all of the
+forward pass: QK^T, masking, online softmax, P.V, normalisation, O and lse
+stores), inputs resident in HBM.  Prints ONE JSON line on stdout; details go
+to stderr.
+
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+                  [--workload n8k_causal_peaky] [--secondary n4k_causal]
+                  [--no-cpu-baseline] [--mode copy]
+
+The headline workload is B=1 H=32 N=8192 d=128 bf16 causal with Q,K x3;
+B=2 H=16 N=4096 d=128 bf16 causal is reported beside it.  FLOP =
+4*B*H*N^2*d, halved when causal.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+TRAFFIC_FILE = ROOT / "profiles" / "fa_fwd_traffic.json"
+KERNEL_SOURCE = ROOT / "io_aware_transformer_amd" / "csrc" / "fa_fwd.hip"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    return hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch from the committed PMC summary, or None when the
+    kernel source changed since the counters were taken."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    rec = json.loads(TRAFFIC_FILE.read_text())
+    if rec.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    if not w:
+        return None
+    return w.get("bytes_per_launch")
+
+
+def time_workload(w, steps: int, warmup: int, seed: int = 0):
+    import torch
+    import io_aware_transformer_amd as fa
+    from io_aware_transformer_amd.inputs import make_workload
+
+    dev = torch.device("cuda", 0)
+    q, k, v = make_workload(w, seed=seed)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    dt = fa.FA_DTYPE_F16 if w.dtype == "f16" else fa.FA_DTYPE_BF16
+
+    def launch():
+        st = fa.fa_fwd(qd, kd, vd, o, lse, w.B, w.H, w.N, w.d, int(w.causal), w.scale, dt,
+                       stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        launch()
+        b.record(stream)
+    t_stop.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    per = sorted(a.elapsed_time(b) for a, b in ev)       # ms, per launch
+    total_ms = t_start.elapsed_time(t_stop)
+    return {
+        "ms_per_step": total_ms / steps,
+        "kernel_ms_mean": sum(per) / len(per),
+        "kernel_ms_median": per[len(per) // 2],
+        "kernel_ms_min": per[0],
+        "wall_s": wall,
+        "inputs": (q, k, v),
+        "outputs": (o, lse),
+    }
+
+
+def cpu_baseline(w, inputs, outputs, target_s: float):
+    """The fp64 oracle on a bounded, evenly spaced sample of query rows of
+    the same workload, timed on the host cores.  The same rows double as a
+    parity sample of the timed GPU output."""
+    import numpy as np
+    import oracle
+    from io_aware_transformer_amd.inputs import bits
+
+    q, k, v = inputs
+    qb, kb, vb = bits(q), bits(k), bits(v)
+    total_rows = w.B * w.H * w.N
+
+    def rows_with_stride(stride, offset=0):
+        return np.arange(offset, total_rows, stride, dtype=np.int64)
+
+    def flops_of(rows):
+        i = rows % w.N
+        keys = (i + 1) if w.causal else np.full(rows.shape, w.N)
+        return float(4.0 * w.d * keys.sum())
+
+    # pilot on ~1/512 of the rows to size the sample
+    pilot = rows_with_stride(512, 7)
+    t0 = time.perf_counter()
+    oracle.attn_fwd_rows(qb, kb, vb, w.dtype, w.causal, w.scale, pilot)
+    t_pilot = time.perf_counter() - t0
+    rate = flops_of(pilot) / max(t_pilot, 1e-6)
+    stride = max(1, int(math.ceil(flops_of(rows_with_stride(1)) / (rate * target_s))))
+    rows = rows_with_stride(stride)
+    t0 = time.perf_counter()
+    ro, rl = oracle.attn_fwd_rows(qb, kb, vb, w.dtype, w.causal, w.scale, rows)
+    secs = time.perf_counter() - t0
+    fl = flops_of(rows)
+    o, lse = outputs
+    og = o.reshape(-1, w.d)[torch_index(rows, o.device)].double().cpu().numpy()
+    lg = lse.reshape(-1)[torch_index(rows, o.device)].double().cpu().numpy()
+    return {
+        "value": fl / secs / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"every {stride}th of the {total_rows} query rows ({rows.size} rows, "
+                   f"{fl:.3e} FLOP) of the same workload, fp64 two-pass oracle, "
+                   f"{secs:.1f} s"),
+        "seconds": secs,
+        "cpu_model": cpu_model(),
+    }, {
+        "rows": int(rows.size),
+        "max_err_o": float(np.abs(og - ro).max()),
+        "max_err_lse": float(np.abs(lg - rl).max()),
+    }
+
+
+def torch_index(rows, device):
+    import torch
+    return torch.from_numpy(rows).to(device)
+
+
+def cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def copy_mode(steps: int) -> None:
+    """A plain elementwise copy of known size (1 GiB read + 1 GiB written),
+    for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy", "bytes_read_per_launch": n * 4,
+                      "bytes_written_per_launch": n * 4, "launches": steps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="n8k_causal_peaky")
+    ap.add_argument("--secondary", default="n4k_causal",
+                    help="second workload reported beside the headline ('none' to skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--mode", choices=["bench", "copy"], default="bench")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              "supported (the forward pass shards over heads without communication, "
+              "so per-GPU throughput is the one-GPU figure).", file=sys.stderr)
+        return 2
+    if args.mode == "copy":
+        copy_mode(args.steps)
+        return 0
+
+    import torch
+    import io_aware_transformer_amd as fa
+    from io_aware_transformer_amd.inputs import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    fa.load()
+    w = WORKLOADS[args.workload]
+    log(f"bench: {w.note}; steps={args.steps} warmup={args.warmup}")
+    res = time_workload(w, args.steps, args.warmup)
+    tflops_step = w.flops / (res["ms_per_step"] * 1e-3) / 1e12
+    achieved = w.flops / (res["kernel_ms_mean"] * 1e-3) / 1e12
+    log(f"bench: {w.name} kernel mean {res['kernel_ms_mean']*1e3:.1f} us, median "
+        f"{res['kernel_ms_median']*1e3:.1f} us, min {res['kernel_ms_min']*1e3:.1f} us, "
+        f"{achieved:.1f} TFLOP/s ({100*achieved/PEAK_BF16_TFLOPS:.1f}% of peak)")
+    traffic = load_traffic(w.name)
+
+    line = {
+        "metric": "attention fwd TFLOP/s and % of MI355X bf16 MFMA peak (N=4K/8K, d=128)",
+        "value": round(tflops_step, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_peak": round(100 * tflops_step / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "qk_gain": w.qk_gain,
+                   "flop_per_step": w.flops},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "fa_fwd_kernel",
+            "kernel_us_mean": round(res["kernel_ms_mean"] * 1e3, 2),
+        },
+    }
+
+    if args.secondary and args.secondary != "none":
+        w2 = WORKLOADS[args.secondary]
+        r2 = time_workload(w2, args.steps, args.warmup)
+        a2 = w2.flops / (r2["kernel_ms_mean"] * 1e-3) / 1e12
+        log(f"bench: {w2.name} kernel mean {r2['kernel_ms_mean']*1e3:.1f} us, "
+            f"{a2:.1f} TFLOP/s ({100*a2/PEAK_BF16_TFLOPS:.1f}% of peak)")
+        line["secondary"] = {"workload": w2.name, "B": w2.B, "H": w2.H, "N": w2.N, "d": w2.d,
+                             "causal": w2.causal, "ms_per_step": round(r2["ms_per_step"], 5),
+                             "tflops": round(w2.flops / (r2["ms_per_step"] * 1e-3) / 1e12, 2),
+                             "kernel_us_mean": round(r2["kernel_ms_mean"] * 1e3, 2),
+                             "frac": round(a2 / PEAK_BF16_TFLOPS, 4)}
+        del r2
+
+    if not args.no_cpu_baseline:
+        cb, par = cpu_baseline(w, res["inputs"], res["outputs"], args.cpu_seconds)
+        log(f"bench: oracle {cb['value']*1e3:.2f} GFLOP/s on {cb['cores']} threads; "
+            f"sampled parity max|dO|={par['max_err_o']:.2e} max|dlse|={par['max_err_lse']:.2e}")
+        line["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        line["cpu_baseline"]["cpu_model"] = cb["cpu_model"]
+        line["parity_sample"] = par
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,89 @@
+/*
+ * fa_fwd.h -- C ABI of the MI355X (gfx950) exact-attention forward pass.
+ *
+ * Operation.  For every batch b, head h and query row i,
+ *     o[b,h,i,:] = sum_j softmax_j(scale * q[b,h,i,:] . k[b,h,j,:]) * v[b,h,j,:]
+ *     lse[b,h,i] = ln sum_j exp(scale * q[b,h,i,:] . k[b,h,j,:])
+ * over the allowed keys j: all j < N, or j <= i when causal (square,
+ * top-left aligned).  This is Attention(Q,K,V) = Softmax(Q K^T / sqrt(d)) V
+ * of "FlashAttention 优化原理与实现要点解析" (cloud.baidu.com) §1, with the
+ * caller's `scale` in place of 1/sqrt(d), and causal masking as in §7 of the
+ * same page.  The N x N score matrix is never written to memory: Q-row tiles
+ * stream K/V tiles through on-chip memory with a running maximum and sum
+ * (§4.2-§6 of that page).  `lse` packs the two per-row statistics that the
+ * kernel signature of "FlashAttention V2 核心原理与架构设计" (wmrh.cn) §2.3
+ * returns separately (row maximum m and denominator l) into lse = m + ln l.
+ *
+ * Layout.  q, k, v and o are contiguous [B,H,N,d] arrays of one 16-bit type
+ * (IEEE binary16 or bfloat16); element (b,h,n,c) is at ((b*H+h)*N+n)*d+c.
+ * lse is a contiguous fp32 [B,H,N] array.  Accumulation is fp32; P is
+ * rounded to the input type (nearest-even) before the P.V product, and o is
+ * rounded to the input type (nearest-even) once, after the division by l.
+ *
+ * Ownership.  Every pointer is a device pointer owned by the caller; the
+ * library allocates nothing and keeps no state between calls, so calls are
+ * reentrant.  q, k and v are only read.  o and lse are fully overwritten
+ * (all B*H*N rows) and must not overlap q, k, v or each other.
+ *
+ * Errors.  Arguments are validated on the host before any HIP call; a
+ * failing call touches no memory and launches nothing.  A passing call
+ * enqueues one kernel on `stream` (0 = the null stream) and returns without
+ * waiting; device faults surface at the caller's next synchronisation.
+ */
+#ifndef FA_FWD_H
+#define FA_FWD_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = -1,  /* null pointer, B/H/N < 1, causal not 0/1,
+                                 non-finite scale, unknown dtype, overlapping
+                                 buffers, or a grid too large to launch */
+    FA_ERR_UNSUPPORTED = -2,  /* d not 64 or 128, or N above FA_MAX_N */
+    FA_ERR_MISALIGNED = -3,   /* q, k, v or o not 16-byte aligned, lse not
+                                 4-byte aligned */
+    FA_ERR_LAUNCH = -4        /* the kernel launch was rejected by HIP */
+} fa_status;
+
+typedef enum { FA_DTYPE_F16 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
+
+/* Largest sequence length accepted (index arithmetic inside one head). */
+#define FA_MAX_N (1 << 24)
+
+/* Forward pass on binary16 tensors.  Arguments as described above:
+ *   q, k, v  [B,H,N,d] binary16, read only
+ *   o        [B,H,N,d] binary16, written
+ *   lse      [B,H,N]   fp32, written (natural log)
+ *   B, H, N  batch, heads, sequence length (>= 1)
+ *   d        head dimension, 64 or 128
+ *   causal   0 = every key, 1 = keys j <= query i
+ *   scale    finite multiplier of q.k (1/sqrt(d) in the usual definition);
+ *            0 and negative values are accepted
+ *   stream   HIP stream the kernel is enqueued on */
+fa_status fa_fwd_f16(const void *q, const void *k, const void *v, void *o,
+                     float *lse, int B, int H, int N, int d, int causal,
+                     float scale, hipStream_t stream);
+
+/* The same on bfloat16 tensors. */
+fa_status fa_fwd_bf16(const void *q, const void *k, const void *v, void *o,
+                      float *lse, int B, int H, int N, int d, int causal,
+                      float scale, hipStream_t stream);
+
+/* The same with the element type given explicitly. */
+fa_status fa_fwd(const void *q, const void *k, const void *v, void *o,
+                 float *lse, int B, int H, int N, int d, int causal,
+                 float scale, fa_dtype dtype, hipStream_t stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_FWD_H */

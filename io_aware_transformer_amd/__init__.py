@@ -1,0 +1,132 @@
+"""Python binding of the MI355X exact-attention forward library (libfa_fwd.so).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels behind the C ABI declared in include/fa_fwd.h.  PyTorch supplies
+device memory and streams.  There is no fallback: if the library cannot be
+loaded (or built with hipcc), every call raises.
+
+C entry points mirrored here with the same names and argument order:
+  fa_fwd_f16(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> status
+  fa_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> status
+  fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream) -> status
+  fa_status_string(status) -> str
+Pointers may be given as integers or as tensors (their data_ptr()); the
+stream as an integer handle, a torch.cuda.Stream, or None (null stream).
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+from .build import LIB as _LIB_PATH, build as _build
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_MISALIGNED = -3
+FA_ERR_LAUNCH = -4
+FA_DTYPE_F16 = 0
+FA_DTYPE_BF16 = 1
+
+EXPORTED = ("fa_fwd_f16", "fa_fwd_bf16", "fa_fwd", "fa_status_string")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"{fa_status_string(status)} (status {status})")
+
+
+def library_path() -> Path:
+    return _LIB_PATH
+
+
+def load():
+    """Load libfa_fwd.so (building it first only if it does not exist)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists():
+        _build()
+    lib = ctypes.CDLL(str(_LIB_PATH))
+    p = ctypes.c_void_p
+    i = ctypes.c_int
+    f = ctypes.c_float
+    sig = [p, p, p, p, p, i, i, i, i, i, f]
+    lib.fa_fwd_f16.argtypes = sig + [p]
+    lib.fa_fwd_bf16.argtypes = sig + [p]
+    lib.fa_fwd.argtypes = sig + [i, p]
+    for n in ("fa_fwd_f16", "fa_fwd_bf16", "fa_fwd"):
+        getattr(lib, n).restype = ctypes.c_int
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def fa_fwd_f16(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None) -> int:
+    return load().fa_fwd_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                             int(N), int(d), int(causal), float(scale), _stream(stream))
+
+
+def fa_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None) -> int:
+    return load().fa_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                              int(N), int(d), int(causal), float(scale), _stream(stream))
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream=None) -> int:
+    return load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                         int(N), int(d), int(causal), float(scale), int(dtype),
+                         _stream(stream))
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None, stream=None):
+    """Allocate o and lse for [B,H,N,d] CUDA tensors q, k, v and run the
+    forward pass on `stream` (default: torch's current stream).
+    Returns (o, lse); raises FaError on a non-zero status."""
+    import torch
+    if q.dtype == torch.float16:
+        dt = FA_DTYPE_F16
+    elif q.dtype == torch.bfloat16:
+        dt = FA_DTYPE_BF16
+    else:
+        raise TypeError("q, k, v must be float16 or bfloat16")
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B,H,N,d] shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous [B,H,N,d]")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd(q, k, v, o, lse, B, H, N, d, int(causal), scale, dt, stream)
+    if st != FA_OK:
+        raise FaError(st)
+    return o, lse

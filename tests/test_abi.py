@@ -1,0 +1,116 @@
+"""CPU tests of the C-ABI library: it loads, exports every function that
+include/fa_fwd.h declares, and rejects bad arguments on the host, before any
+HIP call (so these run without a GPU).  No compute call is made here."""
+from __future__ import annotations
+
+import math
+import re
+import subprocess
+
+import pytest
+
+import io_aware_transformer_amd as fa
+from tests.conftest import ROOT
+
+HEADER = ROOT / "include" / "fa_fwd.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(fa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    fa.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", str(fa.library_path())],
+                         check=True, capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+
+
+def test_status_strings_cover_every_code():
+    for code in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED,
+                 fa.FA_ERR_MISALIGNED, fa.FA_ERR_LAUNCH):
+        s = fa.fa_status_string(code)
+        assert s.startswith(("FA_OK", "FA_ERR_")), s
+    assert fa.fa_status_string(7) == "unknown fa_status"
+
+
+# Fake, well-aligned, non-overlapping device addresses: validation must
+# reject the call before anything dereferences them.
+Q, K, V, O, L = (0x10000 * (i + 1) for i in range(5))
+
+
+def call(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=64, d=128, causal=0, scale=0.125,
+         dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [dict(q=0), dict(k=0), dict(v=0), dict(o=0), dict(lse=0)])
+def test_null_pointers(kw):
+    assert call(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(B=-1), dict(N=-5)])
+def test_non_positive_sizes(kw):
+    assert call(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("causal", [-1, 2, 7])
+def test_causal_flag(causal):
+    assert call(causal=causal) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("scale", [math.inf, -math.inf, math.nan])
+def test_non_finite_scale(scale):
+    assert call(scale=scale) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("dtype", [-1, 2, 99])
+def test_unknown_dtype(dtype):
+    assert call(dtype=dtype) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("d", [1, 32, 63, 96, 127, 256])
+def test_unsupported_head_dim(d):
+    assert call(d=d) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_sequence_too_long():
+    assert call(N=(1 << 24) + 1, q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40,
+                lse=5 << 40) == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(q=Q + 8), dict(k=K + 2), dict(v=V + 4), dict(o=O + 1),
+                                dict(lse=L + 2)])
+def test_misaligned(kw):
+    assert call(**kw) == fa.FA_ERR_MISALIGNED
+
+
+def test_lse_needs_only_4_byte_alignment():
+    # passes validation checks up to the overlap test; with overlapping o it
+    # must still be rejected as INVALID, proving alignment was accepted
+    assert call(lse=L + 4, o=L) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(o=Q), dict(o=K + 64), dict(lse=V + 128), dict(lse=O)])
+def test_overlapping_outputs(kw):
+    assert call(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_typed_entry_points_validate():
+    assert fa.fa_fwd_f16(0, K, V, O, L, 1, 1, 64, 64, 0, 1.0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_fwd_bf16(Q, K, V, O, L, 1, 1, 64, 80, 0, 1.0) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_f16(Q, K, V, O + 2, L, 1, 1, 64, 64, 0, 1.0) == fa.FA_ERR_MISALIGNED
+
+
+def test_grid_too_large():
+    # B*H*ceil(N/128) above INT_MAX is refused on the host
+    assert call(B=1 << 16, H=1 << 16, N=1 << 10, q=1 << 44, k=2 << 44, v=3 << 44,
+                o=4 << 44, lse=5 << 44) == fa.FA_ERR_INVALID_ARG
