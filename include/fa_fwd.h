@@ -52,8 +52,9 @@ typedef enum {
 
 typedef enum { FA_DTYPE_F16 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
 
-/* Largest sequence length accepted (index arithmetic inside one head). */
-#define FA_MAX_N (1 << 24)
+/* Largest sequence length accepted: one head of K or V (N*d*2 bytes) must
+ * stay addressable with 32-bit byte offsets. */
+#define FA_MAX_N (1 << 22)
 
 /* Forward pass on binary16 tensors.  Arguments as described above:
  *   q, k, v  [B,H,N,d] binary16, read only

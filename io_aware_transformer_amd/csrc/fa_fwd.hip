@@ -5,41 +5,47 @@
 //   [P-baidu] "FlashAttention 优化原理与实现要点解析"    (cloud.baidu.com)
 //   [P-wmrh]  "FlashAttention V2 核心原理与架构设计"     (wmrh.cn)
 //
-// What one work-group does.  The grid runs over (batch, head, Q-block)
-// ([P-notes] §五.1: sequence-dimension parallelism).  A work-group owns BR
-// query rows and loops over the K/V tiles with the Q block outer and the K/V
-// block inner ([P-notes] §五.2, [P-wmrh] §2.2 "V2"), so its output tile is
-// accumulated on chip and written once.  Each of its four wavefronts owns a
-// 32-row slab of the queries ([P-notes] §五.3 split-Q): a wave's softmax
-// statistics never leave the wave, and no cross-wave reduction exists.
+// Work decomposition.  The grid runs over (batch, head, Q block)
+// ([P-notes] §五.1: parallelism along the sequence as well).  A work-group
+// owns 128 query rows and walks the K/V tiles of 64 keys with the Q block
+// outer and the K/V block inner ([P-notes] §五.2, [P-wmrh] §2.2 "V2"), so
+// its output is accumulated on chip and written once.  Each of its four
+// wavefronts owns a 32-row slab of the queries ([P-notes] §五.3, split-Q):
+// softmax statistics never leave the wave and no cross-wave reduction exists.
 //
-// Per K/V tile, per wave ([P-baidu] §5, steps 1-4):
-//   S^T = K_j Q_i^T                on MFMA 32x32x16 (16-bit in, fp32 acc)
-//   mask (diagonal / ragged-tail tiles only)
-//   m_new = max(m, rowmax(S) * c)      c = |scale| * log2(e)
-//   alpha = 2^(m - m_new), P = 2^(S*c - m_new)
-//   l = alpha * l + rowsum(P)          ([P-baidu] §4.2)
-//   O^T = alpha * O^T + V_j^T P^T      on MFMA  ([P-baidu] §4.3)
-// and after the last tile O = O / l, lse = (m + log2 l) * ln 2 ([P-baidu]
-// §4.3 and §6: numerator and denominator are kept apart and divided once).
+// Per K/V tile j, per wave ([P-baidu] §5 steps 1-4, §4.2, §4.3):
+//   S^T = K_j Q^T                 MFMA 32x32x16, 16-bit in, fp32 accumulate
+//   mask                          diagonal and ragged-tail tiles only
+//   m' = max(m, rowmax(S) c)      c = |scale| log2(e); log2 domain
+//   P = 2^(S c - m'),  l = 2^(m - m') l + rowsum(P)
+//   O^T = 2^(m - m') O^T + V_j^T P^T      MFMA, P rounded to 16 bits
+// and after the last tile O = O / l, lse = (m + log2 l) ln 2 ([P-baidu] §4.3
+// and §6: numerator and denominator kept apart, one division at the end).
 //
-// Why S^T rather than S: with the 32x32 MFMA's output layout a lane holds 16
-// key positions of ONE query column, and lanes l and l+32 hold the other 16.
-// The row maximum is then a per-lane reduction plus one exchange between the
-// two wave halves, the row sum needs no exchange until the end, and the fp32
-// score registers, once rounded to 16 bits, are already the B operand of the
-// P.V product -- no shuffles between the two MFMAs.
+// MI355X-specific choices (the pages' A100 design is prior art only):
+//  * S^T rather than S.  In the 32x32 MFMA output a lane holds 16 keys of ONE
+//    query column (lane l and l+32 share the column).  Row max and row sum are
+//    per-lane work plus one v_permlane32_swap, and the fp32 scores, once
+//    rounded to 16 bits, are already the B operand of the P.V product.
+//  * Every accumulator lives in VGPRs (about 240 per lane), so two waves share
+//    each SIMD (two work-groups per CU) and the MFMA pipe of one wave overlaps
+//    the softmax VALU work of the other.
+//  * Software pipeline inside the wave as well: the MFMAs of
+//    S(j+1) = K_{j+1} Q^T are issued together with the VALU work of P(j)
+//    (exp, row sum, rounding), and the MFMAs of V_j^T P(j)^T together with
+//    the row max of S(j+1).
+//  * K/V tiles go HBM -> LDS with buffer_load ... lds (no registers, no VALU);
+//    rows past N come back as zeros from the buffer range check.  K is read
+//    with ds_read_b128, V with ds_read_b64_tr_b16, which delivers V^T
+//    fragments directly.  16-byte chunks inside each row are XOR-swizzled so
+//    both read patterns are bank-conflict free.
+//  * The reference maximum m moves only when a tile's maximum exceeds it by
+//    more than 8 (log2 units); then P <= 256 and the result is the same
+//    quotient, while the O rescale (64 multiplies per lane) is almost never
+//    executed.
 //
-// K/V tiles pass through LDS, double buffered: tile j+1 is fetched from HBM
-// into registers with 128-bit loads while tile j is computed, then written to
-// the other LDS buffer.  K is stored [key][d] (its MFMA operand wants d
-// contiguous); V is stored transposed [d][key] (the P.V operand wants keys
-// contiguous).  Both rows are padded so the MFMA-operand reads of a wave hit
-// distinct LDS banks.
-//
-// Causal tiles that lie wholly above the diagonal are never visited
-// ([P-baidu] §7); the last Q block of a ragged N masks keys >= N and does not
-// store rows >= N.
+// Causal K/V tiles wholly above the diagonal are never visited ([P-baidu]
+// §7); the last Q block of a ragged N masks keys >= N and stores no rows >= N.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -52,8 +58,7 @@ namespace {
 
 typedef unsigned short u16;
 typedef u16 u16x8 __attribute__((ext_vector_type(8)));
-typedef u16 u16x4 __attribute__((ext_vector_type(4)));
-typedef u16 u16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -61,13 +66,17 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+#define LDS __attribute__((address_space(3)))
 
 constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBR = 32 * kWaves;   // query rows per work-group
-constexpr int kBC = 64;            // keys per K/V tile
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 32;                 // one 32-column MFMA block
+constexpr int kBR = kWaves * kRowsPerWave;       // query rows per work-group
+constexpr int kBC = 64;                          // keys per K/V tile
+constexpr float kLazy = 8.0f;                    // reference-max slack, log2 units
+constexpr unsigned kRsrcWord3 = 0x00020000u;     // raw buffer, 32-bit data
 
-// Element-type specifics: the MFMA and the fp32 -> 16-bit pair conversion
+// Element-type specifics: the MFMA and fp32 -> 16-bit pair conversion
 // (round to nearest even).
 template <int DT> struct Elem;
 
@@ -80,6 +89,11 @@ template <> struct Elem<FA_DTYPE_F16> {
         f16x2 h = {(_Float16)x, (_Float16)y};
         return __builtin_bit_cast(unsigned, h);
     }
+    // acc + the two 16-bit values of a packed pair (products by 1.0 are exact)
+    static __device__ __forceinline__ float sum2(unsigned pr, float acc) {
+        const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pr), one, acc, false);
+    }
 };
 
 template <> struct Elem<FA_DTYPE_BF16> {
@@ -91,35 +105,65 @@ template <> struct Elem<FA_DTYPE_BF16> {
         bf16x2 h = {(__bf16)x, (__bf16)y};
         return __builtin_bit_cast(unsigned, h);
     }
+    static __device__ __forceinline__ float sum2(unsigned pr, float acc) {
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr), one, acc, false);
+    }
+};
+
+// Geometry of one K or V tile (kBC rows of D 16-bit elements) in LDS: rows
+// are dense, 16-byte chunks inside a row are XOR-swizzled by a function of
+// the row.  K rows: 16 consecutive rows reading one logical chunk (one
+// ds_read_b128 per lane) land on distinct banks.  V rows: the 4 rows x 64
+// bytes that 32 lanes of one transposing read touch land on distinct banks.
+template <int D> struct Tile {
+    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kChunks = D / 8;
+    static constexpr int kBytes = kBC * kRowBytes;
+    static constexpr int kLoadsPerWave = kBytes / 1024 / kWaves;
+    static constexpr int kRowsPerLoad = 1024 / kRowBytes;
+    static __device__ __forceinline__ int kswz(int row) {
+        return D == 128 ? (row & 15) : ((row >> 1) & 7);
+    }
+    static __device__ __forceinline__ int vswz(int row) {
+        return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+    }
 };
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
-// Key position held by accumulator register r of a 32x32 MFMA output in
-// wave half hh (lanes 32*hh .. 32*hh+31): rows 8*(r/4) + 4*hh + r%4.
+// Key (row) position held by accumulator register r of a 32x32 MFMA output
+// in wave half hh: 8*(r/4) + 4*hh + r%4.
 __device__ __forceinline__ int acc_row(int r, int hh) {
     return 8 * (r >> 2) + 4 * hh + (r & 3);
 }
 
+// Value of x in the other half of the wave (lane l <-> l^32), via
+// v_permlane32_swap: swap(x, x) yields [x_lo, x_lo] and [x_hi, x_hi].
+__device__ __forceinline__ float half_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                    const u16 *__restrict__ V, u16 *__restrict__ O,
                    float *__restrict__ LSE, int BH, int N, int nqb, float c,
-                   unsigned qsign)
+                   unsigned qand, unsigned qxor)
 {
     using E = Elem<DT>;
-    constexpr int KP = D + 8;          // K row pitch in LDS (elements)
-    constexpr int VP = kBC + 4;        // V^T row pitch in LDS (elements)
-    constexpr int KSZ = kBC * KP;
-    constexpr int VSZ = D * VP;
-    constexpr int KT = D / 16;         // MFMA k-steps over d for S^T
-    constexpr int DB = D / 32;         // 32-row blocks of O^T
-    constexpr int CPR = D / 8;         // 16-byte chunks per row
-    constexpr int NCH = kBC * CPR / kThreads;   // chunks per thread per tile
-    static_assert(NCH == 2 || NCH == 4, "tile shape");
+    using T = Tile<D>;
+    constexpr int KT = D / 16;    // MFMA k-steps over d
+    constexpr int DB = D / 32;    // 32-row blocks of O^T
+    constexpr int PT = kBC / 16;  // MFMA k-steps over the keys of a tile
 
-    __shared__ __attribute__((aligned(16))) u16 smem[2 * (KSZ + VSZ)];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * T::kBytes];
+    LDS unsigned char *lds = (LDS unsigned char *)smem;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -127,205 +171,243 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     const int l32 = lane & 31;
     const int hh = lane >> 5;
 
-    // Work-group -> (batch*head, Q block).  Heads vary fastest so that, with
-    // work-groups dealt round-robin over the 8 XCDs, every Q block of one head
-    // lands on the same XCD (and L2) whenever B*H is a multiple of 8.  Causal
+    // Work-group -> (batch*head, Q block).  Heads vary fastest: with
+    // work-groups dealt round-robin over the 8 XCDs, all Q blocks of one head
+    // share an XCD (and its L2) whenever B*H is a multiple of 8.  Causal
     // grids start with the longest (last) Q blocks.
     const int L = blockIdx.x;
     const int bh = L % BH;
-    const int qb = CAUSAL ? (nqb - 1 - L / BH) : (L / BH);
+    const int qblk = CAUSAL ? (nqb - 1 - L / BH) : (L / BH);
     const size_t head = (size_t)bh * (size_t)N * D;
-    const u16 *Qh = Q + head;
-    const u16 *Kh = K + head;
-    const u16 *Vh = V + head;
+    const int nbytes = N * T::kRowBytes;
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(Q + head), 0, nbytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(K + head), 0, nbytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(V + head), 0, nbytes, kRsrcWord3);
 
-    const int q_first = qb * kBR + 32 * w;    // first query row of this wave
-    const int qrow = q_first + l32;           // the query row of this lane
-    const bool wave_live = q_first < N;
+    const int q0 = qblk * kBR + kRowsPerWave * w;   // first query row of this wave
+    const int qrow = q0 + l32;                      // the query row of this lane
 
-    // Q slab -> B-operand fragments, kept in registers for the whole loop.
+    // Q slab -> B-operand fragments (rows past N read as zero), kept in
+    // registers for the whole loop.  qand/qxor zero or negate Q exactly.
     u16x8 qf[KT];
 #pragma unroll
     for (int kk = 0; kk < KT; ++kk) {
-        u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (qrow < N)
-            x = *(const u16x8 *)(Qh + (size_t)qrow * D + 16 * kk + 8 * hh);
-        qf[kk] = x ^ (u16)qsign;
+        const int off = (qrow * D + 16 * kk + 8 * hh) * 2;
+        u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+        x = (x & qand) ^ qxor;
+        qf[kk] = __builtin_bit_cast(u16x8, x);
     }
 
-    const int kv_end = CAUSAL ? min(N, (qb + 1) * kBR) : N;
-    const int n_tiles = (kv_end + kBC - 1) / kBC;
+    const int n_keys_tiles = (N + kBC - 1) / kBC;
+    const int n_tiles = CAUSAL ? min(n_keys_tiles, (qblk + 1) * (kBR / kBC)) : n_keys_tiles;
+    // tiles this wave computes: causal rows q0..q0+31 need keys <= q0+31
+    const int n_w = (q0 >= N) ? 0 : (CAUSAL ? min(n_tiles, (q0 + kRowsPerWave - 1) / kBC + 1)
+                                            : n_tiles);
 
-    // ---- K/V tile staging: HBM -> registers -> LDS
-    u16x8 kreg[NCH], vreg[NCH];
-    auto fetch = [&](int t) {
-        const int kv0 = t * kBC;
+    // ---- HBM -> LDS tile loads (each wave moves its share, 1 KB per load)
+    auto issue = [&](const __amdgpu_buffer_rsrc_t &r, int buf, int t, bool is_v) {
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int ci = tid + kThreads * i;
-            const int row = ci / CPR, col8 = ci % CPR;
-            const int key = kv0 + row;
-            u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (key < N) x = *(const u16x8 *)(Kh + (size_t)key * D + col8 * 8);
-            kreg[i] = x;
-        }
-        const int col8 = tid % CPR, kg = tid / CPR;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int key = kv0 + kg * NCH + i;
-            u16x8 x = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (key < N) x = *(const u16x8 *)(Vh + (size_t)key * D + col8 * 8);
-            vreg[i] = x;
+        for (int j = 0; j < T::kLoadsPerWave; ++j) {
+            const int li = w * T::kLoadsPerWave + j;
+            const int row = li * T::kRowsPerLoad + lane / T::kChunks;
+            const int pc = lane % T::kChunks;
+            const int lc = pc ^ (is_v ? T::vswz(row) : T::kswz(row));
+            const int off = (t * kBC + row) * T::kRowBytes + lc * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (LDS void *)(lds + buf * T::kBytes + li * 1024), 16, off, 0, 0, 0);
         }
     };
-    auto stash = [&](int buf) {
-        u16 *Ks = smem + buf * (KSZ + VSZ);
-        u16 *Vs = Ks + KSZ;
+    // buffers: 0,1 = K tiles (j even/odd), 2,3 = V tiles (j even/odd)
+
+    // Per-lane LDS offsets of the MFMA operand reads (loop invariant).
+    int koff[KT];           // K_j: row 32*kb + l32, logical chunk 2*kk + hh
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const int ci = tid + kThreads * i;
-            const int row = ci / CPR, col8 = ci % CPR;
-            *(u16x8 *)(Ks + row * KP + col8 * 8) = kreg[i];
-        }
-        const int col8 = tid % CPR, kg = tid / CPR;
+    for (int kk = 0; kk < KT; ++kk)
+        koff[kk] = l32 * T::kRowBytes + (((2 * kk + hh) ^ T::kswz(l32)) << 4);
+    int voff[DB];           // V_j transposing reads, see the layout note above
+    {
+        const int g = lane >> 4, i = lane & 15;
+        const int row = 4 * (g >> 1) + (i >> 2);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            u16 *dst = Vs + (col8 * 8 + e) * VP + kg * NCH;
-            if constexpr (NCH == 4) {
-                u16x4 t = {vreg[0][e], vreg[1][e], vreg[2][e], vreg[3][e]};
-                *(u16x4 *)dst = t;
-            } else {
-                u16x2 t = {vreg[0][e], vreg[1][e]};
-                *(u16x2 *)dst = t;
-            }
+        for (int db = 0; db < DB; ++db) {
+            const int d = 32 * db + 16 * (g & 1) + 4 * (i & 3);
+            voff[db] = row * T::kRowBytes + (((d >> 3) ^ T::vswz(row)) << 4) + ((d >> 2) & 1) * 8;
         }
+    }
+
+    auto kfrag = [&](int buf, int kb, int kk) -> u16x8 {
+        return *(const LDS u16x8 *)(lds + buf * T::kBytes + kb * 32 * T::kRowBytes + koff[kk]);
+    };
+    auto vfrag = [&](int buf, int db, int kk) -> u16x8 {
+        const LDS unsigned char *p = lds + buf * T::kBytes + kk * 16 * T::kRowBytes + voff[db];
+        const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4 *)p);
+        const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS s16x4 *)(p + 8 * T::kRowBytes));
+        return __builtin_bit_cast(u16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
-    fetch(0);
-    stash(0);
-    __syncthreads();
-
-    float m_run = neg_inf();   // running max, log2 domain (scaled by c)
-    float l_run = 0.f;         // this lane's half of the running sum
-    f32x16 oacc[DB];
+    // S^T(j) = K_j Q^T: s[kb], keys 32*kb.., query column l32
+    auto qk = [&](f32x16 (&s)[2], int buf) {
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+        for (int kk = 0; kk < KT; ++kk)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[b][r] = 0.f;
-
-    for (int t = 0; t < n_tiles; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < n_tiles) fetch(t + 1);
-        const u16 *Ks = smem + buf * (KSZ + VSZ);
-        const u16 *Vs = Ks + KSZ;
-        const int kv0 = t * kBC;
-        const bool active = wave_live && (!CAUSAL || kv0 <= q_first + 31);
-        if (active) {
-            // S^T = K_j Q^T : two 32-key blocks
-            f32x16 s[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < KT; ++kk)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const u16x8 kf =
-                        *(const u16x8 *)(Ks + (32 * kb + l32) * KP + 16 * kk + 8 * hh);
+            for (int kb = 0; kb < 2; ++kb) {
+                const u16x8 kf = kfrag(buf, kb, kk);
+                if (kk == 0) {
+                    const f32x16 z = {};
+                    s[kb] = E::mfma(kf, qf[kk], z);
+                } else {
                     s[kb] = E::mfma(kf, qf[kk], s[kb]);
                 }
-
-            const bool masked = (kv0 + kBC > N) || (CAUSAL && kv0 + kBC - 1 > q_first);
-            if (masked) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kv0 + 32 * kb + acc_row(r, hh);
-                        const bool keep = key < N && (!CAUSAL || key <= qrow);
-                        if (!keep) s[kb][r] = neg_inf();
-                    }
             }
+    };
 
-            // row maximum: in-lane, then across the two wave halves
-            float mx = neg_inf();
+    auto mask = [&](f32x16 (&s)[2], int t) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mt = (mx == neg_inf()) ? neg_inf() : mx * c;
-            const float m_new = fmaxf(m_run, mt);
-            const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-
-            // P = 2^(S*c - m), rounded to 16 bits as the B operand of P.V
-            u32x4 pk[kBC / 16];
-            float rs = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -m_use));
-                    float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -m_use));
-                    if (masked) {
-                        p0 = (s[kb][r] == neg_inf()) ? 0.f : p0;
-                        p1 = (s[kb][r + 1] == neg_inf()) ? 0.f : p1;
-                    }
-                    rs += p0 + p1;
-                    pk[2 * kb + (r >> 3)][(r & 7) >> 1] = E::pack2(p0, p1);
-                }
-            l_run = l_run * alpha + rs;
-            m_run = m_new;
-            if (__ballot(alpha != 1.f)) {
-#pragma unroll
-                for (int b = 0; b < DB; ++b)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[b][r] *= alpha;
+            for (int r = 0; r < 16; ++r) {
+                const int key = t * kBC + 32 * kb + acc_row(r, hh);
+                const bool keep = key < N && (!CAUSAL || key <= qrow);
+                if (!keep) s[kb][r] = neg_inf();
             }
+    };
 
-            // O^T += V_j^T P^T
+    float m = neg_inf();   // reference max, log2 domain
+    float l = 0.f;         // this lane's half of the row sum of P (fp32)
+    float lh = 0.f;        // the same sum of P rounded to 16 bits
+    f32x16 oacc[DB];
 #pragma unroll
-            for (int kk = 0; kk < kBC / 16; ++kk) {
-                const u16x8 pf = __builtin_bit_cast(u16x8, pk[kk]);
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int b = 0; b < DB; ++b) {
-                    const u16 *vp = Vs + (32 * b + l32) * VP + 16 * kk + 4 * hh;
-                    const u16x4 lo = *(const u16x4 *)vp;
-                    const u16x4 hi = *(const u16x4 *)(vp + 8);
-                    const u16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    oacc[b] = E::mfma(vf, pf, oacc[b]);
-                }
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+
+    // Row max of S(j) and the (lazy) update of the reference max.
+    auto update_max = [&](f32x16 (&s)[2]) {
+        float mx = neg_inf();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        const float mt = half_max(mx) * c;
+        if (__builtin_amdgcn_ballot_w64(mt > m + kLazy)) {
+            const float mn = fmaxf(m, mt);
+            const float mu = (mn == neg_inf()) ? 0.f : mn;
+            const float alpha = __builtin_amdgcn_exp2f(m - mu);
+            l *= alpha;
+            lh *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            m = mn;
+        }
+    };
+
+    // P(j) = 2^(S c - m) rounded to 16 bits (B operand of P.V), row sums.
+    // O is divided by the sum of the ROUNDED weights, so the weights applied
+    // to V stay a convex combination (the rounding of a dominant weight
+    // cancels); lse uses the fp32 sum.
+    auto softmax = [&](f32x16 (&s)[2], u32x4 (&pk)[PT]) {
+        const float mu = (m == neg_inf()) ? 0.f : m;
+        float rs = 0.f, rh = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mu));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -mu));
+                rs += p0;
+                rs += p1;
+                const unsigned pr = E::pack2(p0, p1);
+                rh = E::sum2(pr, rh);
+                pk[2 * kb + (r >> 3)][(r & 7) >> 1] = pr;
+            }
+        l += rs;
+        lh += rh;
+    };
+
+    // O^T += V_j^T P(j)^T
+    auto pv = [&](int buf, u32x4 (&pk)[PT]) {
+#pragma unroll
+        for (int kk = 0; kk < PT; ++kk)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                oacc[db] = E::mfma(vfrag(buf, db, kk), __builtin_bit_cast(u16x8, pk[kk]), oacc[db]);
+    };
+
+    auto tile_masked = [&](int t) {
+        return (CAUSAL && t * kBC + kBC - 1 > q0) || (t * kBC + kBC > N);
+    };
+
+    // ---- prologue: K_0, V_0, K_1 in flight; S(0)
+    issue(rk, 0, 0, false);
+    issue(rv, 2, 0, true);
+    if (n_tiles > 1) issue(rk, 1, 1, false);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    f32x16 sA[2], sB[2];
+    if (n_w > 0) {
+        qk(sA, 0);
+        if (tile_masked(0)) mask(sA, 0);
+        update_max(sA);
+    }
+    __syncthreads();   // K_0 fully consumed before K_2 overwrites buffer 0
+
+    // One tile step: P(t) from scur, S(t+1) into snext, O += V_t P(t).
+    auto step = [&](int t, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+        if (t + 2 < n_tiles) issue(rk, t & 1, t + 2, false);
+        if (t + 1 < n_tiles) issue(rv, 2 + ((t + 1) & 1), t + 1, true);
+        if (t < n_w) {
+            u32x4 pk[PT];
+            if (t + 1 < n_w) {
+                qk(snext, (t + 1) & 1);
+                softmax(scur, pk);
+                pv(2 + (t & 1), pk);
+                if (tile_masked(t + 1)) mask(snext, t + 1);
+                update_max(snext);
+            } else {
+                softmax(scur, pk);
+                pv(2 + (t & 1), pk);
             }
         }
-        if (t + 1 < n_tiles) stash(buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+
+    for (int t = 0; t < n_tiles; t += 2) {
+        step(t, sA, sB);
+        if (t + 1 < n_tiles) step(t + 1, sB, sA);
     }
 
     // ---- epilogue: one division per row, 16-bit O, fp32 lse
-    if (wave_live) {
-        const float lt = l_run + __shfl_xor(l_run, 32);
+    if (n_w > 0) {
+        const float lt = half_sum(l);
+        const float lht = half_sum(lh);
         if (qrow < N) {
-            const float inv = 1.f / lt;
+            const float inv = 1.f / lht;
             u16 *orow = O + head + (size_t)qrow * D;
 #pragma unroll
-            for (int b = 0; b < DB; ++b)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     u32x2 pr;
-                    pr[0] = E::pack2(oacc[b][4 * g] * inv, oacc[b][4 * g + 1] * inv);
-                    pr[1] = E::pack2(oacc[b][4 * g + 2] * inv, oacc[b][4 * g + 3] * inv);
-                    *(u32x2 *)(orow + 32 * b + 8 * g + 4 * hh) = pr;
+                    pr[0] = E::pack2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+                    pr[1] = E::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+                    *(u32x2 *)(orow + 32 * db + 8 * g + 4 * hh) = pr;
                 }
             if (hh == 0)
-                LSE[(size_t)bh * N + qrow] = (m_run + log2f(lt)) * 0.69314718055994530942f;
+                LSE[(size_t)bh * N + qrow] = (m + log2f(lt)) * 0.69314718055994530942f;
         }
     }
 }
 
 typedef void (*kernel_fn)(const u16 *, const u16 *, const u16 *, u16 *, float *,
-                          int, int, int, float, unsigned);
+                          int, int, int, float, unsigned, unsigned);
 
 template <int DT>
 kernel_fn pick(int d, int causal)
@@ -371,17 +453,18 @@ extern "C" fa_status fa_fwd(const void *q, const void *k, const void *v, void *o
 
     kernel_fn fn = (dtype == FA_DTYPE_F16) ? pick<FA_DTYPE_F16>(d, causal)
                                            : pick<FA_DTYPE_BF16>(d, causal);
-    // scale < 0: negate Q exactly (flip its sign bits) and use |scale|, so the
-    // running maximum is always taken over non-negatively scaled scores.
-    const float c = fabsf(scale) * 1.44269504088896340736f;   // log2(e)
-    const unsigned qsign = (scale < 0.f) ? 0x8000u : 0u;
+    // Scores are always taken with a positive multiplier c: scale < 0 negates
+    // Q exactly (sign bits) and scale == 0 zeroes Q (every score 0, every
+    // allowed key weighted equally); c = |scale| log2(e), or log2(e) for 0.
+    const float mag = (scale == 0.f) ? 1.f : fabsf(scale);
+    float c = mag * 1.44269504088896340736f;
+    unsigned qand = (scale == 0.f) ? 0u : 0xffffffffu;
+    unsigned qxor = (scale < 0.f) ? 0x80008000u : 0u;
     int bh_i = (int)BH, n_i = N, nqb_i = (int)nqb;
-    float c_f = c;
-    unsigned qs = qsign;
     const void *qp = q, *kp = k, *vp = v;
     void *op = o;
     float *lp = lse;
-    void *args[] = {&qp, &kp, &vp, &op, &lp, &bh_i, &n_i, &nqb_i, &c_f, &qs};
+    void *args[] = {&qp, &kp, &vp, &op, &lp, &bh_i, &n_i, &nqb_i, &c, &qand, &qxor};
     hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)grid), dim3(kThreads),
                                    args, 0, stream);
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -408,7 +491,7 @@ extern "C" const char *fa_status_string(int status)
     case FA_ERR_INVALID_ARG:
         return "FA_ERR_INVALID_ARG: null pointer, non-positive size, causal not 0/1, "
                "non-finite scale, unknown dtype, overlapping buffers or grid too large";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 64 or 128, N <= 2^24";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head dim must be 64 or 128, N <= 2^22";
     case FA_ERR_MISALIGNED:
         return "FA_ERR_MISALIGNED: q/k/v/o need 16-byte alignment, lse 4-byte";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: HIP rejected the kernel launch";

@@ -83,7 +83,7 @@ def test_unsupported_head_dim(d):
 
 
 def test_sequence_too_long():
-    assert call(N=(1 << 24) + 1, q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40,
+    assert call(N=(1 << 22) + 1, q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40,
                 lse=5 << 40) == fa.FA_ERR_UNSUPPORTED
 
 
