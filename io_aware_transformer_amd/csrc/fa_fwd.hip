@@ -27,13 +27,17 @@
 //    query column (lane l and l+32 share the column).  Row max and row sum are
 //    per-lane work plus one v_permlane32_swap, and the fp32 scores, once
 //    rounded to 16 bits, are already the B operand of the P.V product.
-//  * Every accumulator lives in VGPRs (about 240 per lane), so two waves share
-//    each SIMD (two work-groups per CU) and the MFMA pipe of one wave overlaps
-//    the softmax VALU work of the other.
-//  * Software pipeline inside the wave as well: the MFMAs of
-//    S(j+1) = K_{j+1} Q^T are issued together with the VALU work of P(j)
-//    (exp, row sum, rounding), and the MFMAs of V_j^T P(j)^T together with
-//    the row max of S(j+1).
+//  * Every accumulator lives in VGPRs (about 200 per lane), so two waves share
+//    each SIMD (two work-groups per CU, each with its own barriers) and the
+//    MFMA pipe of one wave overlaps the softmax VALU work of the other.
+//    Measured on MI355X: a single wave that interleaves LDS operand reads
+//    with its MFMAs sustains ~44 cycles per 32-cycle MFMA, two such waves per
+//    SIMD ~37.5, so the MFMA work must come from two waves at once.  (Both an
+//    in-wave software pipeline, S(j+1) on MFMA while P(j) is on VALU, and a
+//    barrier-enforced A/B phase offset between the two waves of a SIMD
+//    measured slower than letting two work-groups drift freely.)
+//  * Reductions over a row (max, fp32 sum, rounded sum) run as short trees
+//    or several independent chains, never one serial dependency chain.
 //  * K/V tiles go HBM -> LDS with buffer_load ... lds (no registers, no VALU);
 //    rows past N come back as zeros from the buffer range check.  K is read
 //    with ds_read_b128, V with ds_read_b64_tr_b16, which delivers V^T
@@ -132,6 +136,12 @@ template <int D> struct Tile {
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// Compile-time buffer index (the K/V LDS buffers are separate objects and
+// always selected statically, so the compiler can tell that the HBM->LDS
+// prefetch of one buffer does not alias the reads of another and need not
+// wait for it).
+template <int I> struct Buf { static constexpr int value = I; };
+
 // Key (row) position held by accumulator register r of a 32x32 MFMA output
 // in wave half hh: 8*(r/4) + 4*hh + r%4.
 __device__ __forceinline__ int acc_row(int r, int hh) {
@@ -162,12 +172,23 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     constexpr int DB = D / 32;    // 32-row blocks of O^T
     constexpr int PT = kBC / 16;  // MFMA k-steps over the keys of a tile
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * T::kBytes];
-    LDS unsigned char *lds = (LDS unsigned char *)smem;
+    __shared__ __attribute__((aligned(1024))) unsigned char k0s[T::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char k1s[T::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char v0s[T::kBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char v1s[T::kBytes];
+    // buffers: 0,1 = K tiles (j even/odd), 2,3 = V tiles (j even/odd)
+    auto bufp = [&](auto b) -> LDS unsigned char * {
+        constexpr int i = decltype(b)::value;
+        if constexpr (i == 0) return (LDS unsigned char *)k0s;
+        else if constexpr (i == 1) return (LDS unsigned char *)k1s;
+        else if constexpr (i == 2) return (LDS unsigned char *)v0s;
+        else return (LDS unsigned char *)v1s;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    // wave index as a scalar: every per-wave decision below is a scalar branch
+    const int w = (tid >> 6);
     const int l32 = lane & 31;
     const int hh = lane >> 5;
 
@@ -208,7 +229,8 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                                             : n_tiles);
 
     // ---- HBM -> LDS tile loads (each wave moves its share, 1 KB per load)
-    auto issue = [&](const __amdgpu_buffer_rsrc_t &r, int buf, int t, bool is_v) {
+    auto issue = [&](const __amdgpu_buffer_rsrc_t &r, auto buf, int t) {
+        constexpr bool is_v = decltype(buf)::value >= 2;
 #pragma unroll
         for (int j = 0; j < T::kLoadsPerWave; ++j) {
             const int li = w * T::kLoadsPerWave + j;
@@ -217,10 +239,9 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             const int lc = pc ^ (is_v ? T::vswz(row) : T::kswz(row));
             const int off = (t * kBC + row) * T::kRowBytes + lc * 16;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (LDS void *)(lds + buf * T::kBytes + li * 1024), 16, off, 0, 0, 0);
+                r, (LDS void *)(bufp(buf) + li * 1024), 16, off, 0, 0, 0);
         }
     };
-    // buffers: 0,1 = K tiles (j even/odd), 2,3 = V tiles (j even/odd)
 
     // Per-lane LDS offsets of the MFMA operand reads (loop invariant).
     int koff[KT];           // K_j: row 32*kb + l32, logical chunk 2*kk + hh
@@ -238,31 +259,44 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         }
     }
 
-    auto kfrag = [&](int buf, int kb, int kk) -> u16x8 {
-        return *(const LDS u16x8 *)(lds + buf * T::kBytes + kb * 32 * T::kRowBytes + koff[kk]);
+    auto kfrag = [&](auto buf, int kb, int kk) -> u16x8 {
+        return *(const LDS u16x8 *)(bufp(buf) + kb * 32 * T::kRowBytes + koff[kk]);
     };
-    auto vfrag = [&](int buf, int db, int kk) -> u16x8 {
-        const LDS unsigned char *p = lds + buf * T::kBytes + kk * 16 * T::kRowBytes + voff[db];
+    auto vfrag = [&](auto buf, int db, int kk) -> u16x8 {
+        const LDS unsigned char *p = bufp(buf) + kk * 16 * T::kRowBytes + voff[db];
         const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4 *)p);
         const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (LDS s16x4 *)(p + 8 * T::kRowBytes));
         return __builtin_bit_cast(u16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
-    // S^T(j) = K_j Q^T: s[kb], keys 32*kb.., query column l32
-    auto qk = [&](f32x16 (&s)[2], int buf) {
+    // S^T(j) = K_j Q^T: s[kb], keys 32*kb.., query column l32.  Operands
+    // are read from LDS kDepth k-steps ahead of their MFMAs.
+    constexpr int kDepth = 2;
+    auto qk = [&](f32x16 (&s)[2], auto buf) {
+        u16x8 kf[kDepth + 1][2];
 #pragma unroll
-        for (int kk = 0; kk < KT; ++kk)
+        for (int i = 0; i < kDepth; ++i) {
+            kf[i][0] = kfrag(buf, 0, i);
+            kf[i][1] = kfrag(buf, 1, i);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk) {
+            if (kk + kDepth < KT) {
+                kf[(kk + kDepth) % (kDepth + 1)][0] = kfrag(buf, 0, kk + kDepth);
+                kf[(kk + kDepth) % (kDepth + 1)][1] = kfrag(buf, 1, kk + kDepth);
+            }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const u16x8 kf = kfrag(buf, kb, kk);
+                const u16x8 a = kf[kk % (kDepth + 1)][kb];
                 if (kk == 0) {
                     const f32x16 z = {};
-                    s[kb] = E::mfma(kf, qf[kk], z);
+                    s[kb] = E::mfma(a, qf[kk], z);
                 } else {
-                    s[kb] = E::mfma(kf, qf[kk], s[kb]);
+                    s[kb] = E::mfma(a, qf[kk], s[kb]);
                 }
             }
+        }
     };
 
     auto mask = [&](f32x16 (&s)[2], int t) {
@@ -287,11 +321,19 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
     // Row max of S(j) and the (lazy) update of the reference max.
     auto update_max = [&](f32x16 (&s)[2]) {
-        float mx = neg_inf();
+        // 32 values -> 11 -> 4 -> 1 with three-input maxima (depth 4)
+        float t1[11];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        for (int i = 0; i < 10; ++i) {
+            const int a = 3 * i, b = 3 * i + 1, e = 3 * i + 2;
+            t1[i] = fmaxf(fmaxf(s[a >> 4][a & 15], s[b >> 4][b & 15]), s[e >> 4][e & 15]);
+        }
+        t1[10] = fmaxf(s[1][14], s[1][15]);
+        const float u0 = fmaxf(fmaxf(t1[0], t1[1]), t1[2]);
+        const float u1 = fmaxf(fmaxf(t1[3], t1[4]), t1[5]);
+        const float u2 = fmaxf(fmaxf(t1[6], t1[7]), t1[8]);
+        const float u3 = fmaxf(t1[9], t1[10]);
+        const float mx = fmaxf(fmaxf(fmaxf(u0, u1), u2), u3);
         const float mt = half_max(mx) * c;
         if (__builtin_amdgcn_ballot_w64(mt > m + kLazy)) {
             const float mn = fmaxf(m, mt);
@@ -313,66 +355,78 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     // cancels); lse uses the fp32 sum.
     auto softmax = [&](f32x16 (&s)[2], u32x4 (&pk)[PT]) {
         const float mu = (m == neg_inf()) ? 0.f : m;
-        float rs = 0.f, rh = 0.f;
+        float rs[4] = {0.f, 0.f, 0.f, 0.f}, rh[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
+                const int ch = (r >> 1) & 3;      // four independent chains
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mu));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -mu));
-                rs += p0;
-                rs += p1;
+                rs[ch] += p0;
+                rs[ch] += p1;
                 const unsigned pr = E::pack2(p0, p1);
-                rh = E::sum2(pr, rh);
+                rh[ch] = E::sum2(pr, rh[ch]);
                 pk[2 * kb + (r >> 3)][(r & 7) >> 1] = pr;
             }
-        l += rs;
-        lh += rh;
+        l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        lh += (rh[0] + rh[1]) + (rh[2] + rh[3]);
     };
 
-    // O^T += V_j^T P(j)^T
-    auto pv = [&](int buf, u32x4 (&pk)[PT]) {
+    // O^T += V_j^T P(j)^T, operands prefetched 2*kDepth MFMAs ahead
+    auto pv = [&](auto buf, u32x4 (&pk)[PT]) {
+        constexpr int NM = PT * DB;        // MFMAs, index i -> kk = i / DB, db = i % DB
+        constexpr int AHEAD = 2 * kDepth;
+        u16x8 vf[AHEAD + 1];
 #pragma unroll
-        for (int kk = 0; kk < PT; ++kk)
+        for (int i = 0; i < AHEAD; ++i) vf[i] = vfrag(buf, i % DB, i / DB);
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-                oacc[db] = E::mfma(vfrag(buf, db, kk), __builtin_bit_cast(u16x8, pk[kk]), oacc[db]);
+        for (int i = 0; i < NM; ++i) {
+            if (i + AHEAD < NM)
+                vf[(i + AHEAD) % (AHEAD + 1)] = vfrag(buf, (i + AHEAD) % DB, (i + AHEAD) / DB);
+            oacc[i % DB] = E::mfma(vf[i % (AHEAD + 1)],
+                                   __builtin_bit_cast(u16x8, pk[i / DB]), oacc[i % DB]);
+        }
     };
 
     auto tile_masked = [&](int t) {
-        return (CAUSAL && t * kBC + kBC - 1 > q0) || (t * kBC + kBC > N);
+        const bool mk = (CAUSAL && t * kBC + kBC - 1 > q0) || (t * kBC + kBC > N);
+        return __builtin_amdgcn_readfirstlane((int)mk) != 0;
     };
 
     // ---- prologue: K_0, V_0, K_1 in flight; S(0)
-    issue(rk, 0, 0, false);
-    issue(rv, 2, 0, true);
-    if (n_tiles > 1) issue(rk, 1, 1, false);
+    issue(rk, Buf<0>{}, 0);
+    issue(rv, Buf<2>{}, 0);
+    if (n_tiles > 1) issue(rk, Buf<1>{}, 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     f32x16 sA[2], sB[2];
     if (n_w > 0) {
-        qk(sA, 0);
+        qk(sA, Buf<0>{});
         if (tile_masked(0)) mask(sA, 0);
         update_max(sA);
     }
     __syncthreads();   // K_0 fully consumed before K_2 overwrites buffer 0
 
-    // One tile step: P(t) from scur, S(t+1) into snext, O += V_t P(t).
-    auto step = [&](int t, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
-        if (t + 2 < n_tiles) issue(rk, t & 1, t + 2, false);
-        if (t + 1 < n_tiles) issue(rv, 2 + ((t + 1) & 1), t + 1, true);
+    // One tile step (t has parity P): P(t) from scur, O += V_t P(t), then
+    // S(t+1) into snext; meanwhile K_{t+2} and V_{t+1} stream into the
+    // buffers that step t-1 finished with.
+    auto step = [&](auto par, int t, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+        constexpr int P = decltype(par)::value;
+        if (t + 2 < n_tiles) issue(rk, Buf<P>{}, t + 2);
+        if (t + 1 < n_tiles) issue(rv, Buf<3 - P>{}, t + 1);
         if (t < n_w) {
             u32x4 pk[PT];
             if (t + 1 < n_w) {
-                qk(snext, (t + 1) & 1);
                 softmax(scur, pk);
-                pv(2 + (t & 1), pk);
+                pv(Buf<2 + P>{}, pk);
+                qk(snext, Buf<1 - P>{});
                 if (tile_masked(t + 1)) mask(snext, t + 1);
                 update_max(snext);
             } else {
                 softmax(scur, pk);
-                pv(2 + (t & 1), pk);
+                pv(Buf<2 + P>{}, pk);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);
@@ -380,8 +434,8 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     };
 
     for (int t = 0; t < n_tiles; t += 2) {
-        step(t, sA, sB);
-        if (t + 1 < n_tiles) step(t + 1, sB, sA);
+        step(Buf<0>{}, t, sA, sB);
+        if (t + 1 < n_tiles) step(Buf<1>{}, t + 1, sB, sA);
     }
 
     // ---- epilogue: one division per row, 16-bit O, fp32 lse
