@@ -339,7 +339,7 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             const float mn = fmaxf(m, mt);
             const float mu = (mn == neg_inf()) ? 0.f : mn;
             const float alpha = __builtin_amdgcn_exp2f(m - mu);
-            l *= alpha;
+            if constexpr (DT == FA_DTYPE_BF16) l *= alpha;
             lh *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
@@ -352,24 +352,35 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     // P(j) = 2^(S c - m) rounded to 16 bits (B operand of P.V), row sums.
     // O is divided by the sum of the ROUNDED weights, so the weights applied
     // to V stay a convex combination (the rounding of a dominant weight
-    // cancels); lse uses the fp32 sum.
+    // cancels).  lse uses the fp32 sum for bfloat16; for binary16 the
+    // rounded sum is within 2^-11 relative of it (|lse error| <= 4.9e-4),
+    // so it serves for both.
     auto softmax = [&](f32x16 (&s)[2], u32x4 (&pk)[PT]) {
         const float mu = (m == neg_inf()) ? 0.f : m;
-        float rs[4] = {0.f, 0.f, 0.f, 0.f}, rh[4] = {0.f, 0.f, 0.f, 0.f};
+        float rs[4], rh[4];
+        // groups of 8 scores: 8 FMAs, 8 exps, then sums and packing, so the
+        // temporaries die inside the group (scheduling barrier per group)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int g = 0; g < 4; ++g) {
+            const int kb = g >> 1, r0 = (g & 1) * 8;
+            float x[8], p[8];
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const int ch = (r >> 1) & 3;      // four independent chains
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c, -mu));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][r + 1], c, -mu));
-                rs[ch] += p0;
-                rs[ch] += p1;
-                const unsigned pr = E::pack2(p0, p1);
-                rh[ch] = E::sum2(pr, rh[ch]);
-                pk[2 * kb + (r >> 3)][(r & 7) >> 1] = pr;
+            for (int e = 0; e < 8; ++e) x[e] = fmaf(s[kb][r0 + e], c, -mu);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(x[e]);
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                if constexpr (DT == FA_DTYPE_BF16) {
+                    const float a = p[2 * h] + p[2 * h + 1];
+                    rs[h] = (g == 0) ? a : rs[h] + a;
+                }
+                const unsigned pr = E::pack2(p[2 * h], p[2 * h + 1]);
+                rh[h] = E::sum2(pr, (g == 0) ? 0.f : rh[h]);
+                pk[2 * kb + (r0 >> 3)][h] = pr;
             }
-        l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (DT == FA_DTYPE_BF16) l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
         lh += (rh[0] + rh[1]) + (rh[2] + rh[3]);
     };
 
@@ -420,8 +431,12 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             u32x4 pk[PT];
             if (t + 1 < n_w) {
                 softmax(scur, pk);
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(2);
                 pv(Buf<2 + P>{}, pk);
+                __builtin_amdgcn_sched_barrier(0);
                 qk(snext, Buf<1 - P>{});
+                __builtin_amdgcn_s_setprio(0);
                 if (tile_masked(t + 1)) mask(snext, t + 1);
                 update_max(snext);
             } else {
@@ -440,8 +455,8 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
     // ---- epilogue: one division per row, 16-bit O, fp32 lse
     if (n_w > 0) {
-        const float lt = half_sum(l);
         const float lht = half_sum(lh);
+        const float lt = (DT == FA_DTYPE_BF16) ? half_sum(l) : lht;
         if (qrow < N) {
             const float inv = 1.f / lht;
             u16 *orow = O + head + (size_t)qrow * D;
