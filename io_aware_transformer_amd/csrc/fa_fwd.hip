@@ -7,19 +7,21 @@
 //
 // Work decomposition.  The grid runs over (batch, head, Q block)
 // ([P-notes] §五.1: parallelism along the sequence as well).  A work-group
-// owns 128 query rows and walks the K/V tiles of 64 keys with the Q block
-// outer and the K/V block inner ([P-notes] §五.2, [P-wmrh] §2.2 "V2"), so
-// its output is accumulated on chip and written once.  Each of its four
-// wavefronts owns a 32-row slab of the queries ([P-notes] §五.3, split-Q):
-// softmax statistics never leave the wave and no cross-wave reduction exists.
+// owns 256 query rows and walks the keys with the Q block outer and the K/V
+// block inner ([P-notes] §五.2, [P-wmrh] §2.2 "V2"), so its output is
+// accumulated on chip and written once.  Each of its eight wavefronts owns a
+// 32-row slab of the queries ([P-notes] §五.3, split-Q): softmax statistics
+// never leave the wave and no cross-wave reduction exists.  K/V move through
+// LDS in tiles of 128 keys, double buffered, and each tile is consumed as
+// two compute steps of 64 keys.
 //
-// Per K/V tile j, per wave ([P-baidu] §5 steps 1-4, §4.2, §4.3):
+// Per 64-key step j, per wave ([P-baidu] §5 steps 1-4, §4.2, §4.3):
 //   S^T = K_j Q^T                 MFMA 32x32x16, 16-bit in, fp32 accumulate
-//   mask                          diagonal and ragged-tail tiles only
+//   mask                          diagonal and ragged-tail steps only
 //   m' = max(m, rowmax(S) c)      c = |scale| log2(e); log2 domain
 //   P = 2^(S c - m'),  l = 2^(m - m') l + rowsum(P)
 //   O^T = 2^(m - m') O^T + V_j^T P^T      MFMA, P rounded to 16 bits
-// and after the last tile O = O / l, lse = (m + log2 l) ln 2 ([P-baidu] §4.3
+// and after the last step O = O / l, lse = (m + log2 l) ln 2 ([P-baidu] §4.3
 // and §6: numerator and denominator kept apart, one division at the end).
 //
 // MI355X-specific choices (the pages' A100 design is prior art only):
@@ -27,26 +29,31 @@
 //    query column (lane l and l+32 share the column).  Row max and row sum are
 //    per-lane work plus one v_permlane32_swap, and the fp32 scores, once
 //    rounded to 16 bits, are already the B operand of the P.V product.
-//  * Every accumulator lives in VGPRs (about 200 per lane), so two waves share
-//    each SIMD (two work-groups per CU, each with its own barriers) and the
-//    MFMA pipe of one wave overlaps the softmax VALU work of the other.
-//    Measured on MI355X: a single wave that interleaves LDS operand reads
-//    with its MFMAs sustains ~44 cycles per 32-cycle MFMA, two such waves per
-//    SIMD ~37.5, so the MFMA work must come from two waves at once.  (Both an
-//    in-wave software pipeline, S(j+1) on MFMA while P(j) is on VALU, and a
-//    barrier-enforced A/B phase offset between the two waves of a SIMD
-//    measured slower than letting two work-groups drift freely.)
-//  * Reductions over a row (max, fp32 sum, rounded sum) run as short trees
-//    or several independent chains, never one serial dependency chain.
+//  * Every accumulator lives in VGPRs (about 210 per lane), so two waves
+//    share each SIMD and the MFMA work of one overlaps the softmax VALU work
+//    of the other.  One 8-wave work-group fills a CU (128 KB of LDS); the
+//    128-key tiles halve the barriers per key against 64-key tiles.
+//    Measured on MI355X and rejected: 4-wave work-groups (two per CU), a
+//    12-wave group at three waves per SIMD, an in-wave software pipeline
+//    (S(j+1) on MFMA under softmax(j)), and a V^T copy of each tile in LDS
+//    for b128 operand reads (its extra barrier cost more than it saved).
+//  * MFMA operand reads from LDS are issued a fixed number of MFMAs ahead
+//    and the interleave is pinned with scheduling-group barriers; left
+//    alone, the scheduler moves each read next to its MFMA and the wave
+//    stalls on LDS latency.
 //  * K/V tiles go HBM -> LDS with buffer_load ... lds (no registers, no VALU);
-//    rows past N come back as zeros from the buffer range check.  K is read
-//    with ds_read_b128, V with ds_read_b64_tr_b16, which delivers V^T
-//    fragments directly.  16-byte chunks inside each row are XOR-swizzled so
-//    both read patterns are bank-conflict free.
-//  * The reference maximum m moves only when a tile's maximum exceeds it by
+//    rows past N come back as zeros from the buffer range check.  Each wave's
+//    share of the next tile's loads is spread over the MFMAs of the tile's
+//    first QK^T rather than queued all at once, which stalled every wave on
+//    the vector-memory path at the start of each tile.  K is read with
+//    ds_read_b128, V with ds_read_b64_tr_b16, which delivers V^T fragments
+//    directly.  16-byte chunks inside each row are XOR-swizzled so both read
+//    patterns are bank-conflict free.
+//  * The reference maximum m moves only when a step's maximum exceeds it by
 //    more than 8 (log2 units); then P <= 256 and the result is the same
 //    quotient, while the O rescale (64 multiplies per lane) is almost never
-//    executed.
+//    executed.  Row reductions run as trees (v_max3) or several independent
+//    chains, never one serial dependency chain.
 //
 // Causal K/V tiles wholly above the diagonal are never visited ([P-baidu]
 // §7); the last Q block of a ragged N masks keys >= N and stores no rows >= N.
@@ -72,12 +79,16 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 #define LDS __attribute__((address_space(3)))
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;                 // one 32-column MFMA block
 constexpr int kBR = kWaves * kRowsPerWave;       // query rows per work-group
-constexpr int kBC = 64;                          // keys per K/V tile
+constexpr int kBC = 64;                          // keys per compute step
+constexpr int kLT = 128;                         // keys per LDS tile
+constexpr int kNSub = kLT / kBC;                 // compute steps per LDS tile
 constexpr float kLazy = 8.0f;                    // reference-max slack, log2 units
+constexpr int kQkAhead = 4;                      // K operand reads in flight (MFMAs)
+constexpr int kPvAhead = 3;                      // V operand reads in flight (MFMAs)
 constexpr unsigned kRsrcWord3 = 0x00020000u;     // raw buffer, 32-bit data
 
 // Element-type specifics: the MFMA and fp32 -> 16-bit pair conversion
@@ -115,7 +126,7 @@ template <> struct Elem<FA_DTYPE_BF16> {
     }
 };
 
-// Geometry of one K or V tile (kBC rows of D 16-bit elements) in LDS: rows
+// Geometry of one K or V tile (kLT rows of D 16-bit elements) in LDS: rows
 // are dense, 16-byte chunks inside a row are XOR-swizzled by a function of
 // the row.  K rows: 16 consecutive rows reading one logical chunk (one
 // ds_read_b128 per lane) land on distinct banks.  V rows: the 4 rows x 64
@@ -123,8 +134,9 @@ template <> struct Elem<FA_DTYPE_BF16> {
 template <int D> struct Tile {
     static constexpr int kRowBytes = 2 * D;
     static constexpr int kChunks = D / 8;
-    static constexpr int kBytes = kBC * kRowBytes;
-    static constexpr int kLoadsPerWave = kBytes / 1024 / kWaves;
+    static constexpr int kBytes = kLT * kRowBytes;
+    static constexpr int kLoads = kBytes / 1024;                       // 1 KB loads per tile
+    static constexpr int kLoadsPerWave = kLoads / kWaves;
     static constexpr int kRowsPerLoad = 1024 / kRowBytes;
     static __device__ __forceinline__ int kswz(int row) {
         return D == 128 ? (row & 15) : ((row >> 1) & 7);
@@ -141,6 +153,38 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 // prefetch of one buffer does not alias the reads of another and need not
 // wait for it).
 template <int I> struct Buf { static constexpr int value = I; };
+template <bool B> struct Flag { static constexpr bool value = B; };
+
+// v_max3_f32 / v_max_f32 without the input canonicalisation the compiler
+// adds to fmaxf in IEEE mode (scores are never signalling NaNs).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float max2(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// Maximum of N values as a tree of three-input maxima (depth log3 N).
+template <int N> struct TreeMax {
+    static __device__ __forceinline__ float of(const float (&a)[N]) {
+        constexpr int M = (N + 2) / 3;
+        float b[M];
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            if (3 * i + 2 < N) b[i] = max3(a[3 * i], a[3 * i + 1], a[3 * i + 2]);
+            else if (3 * i + 1 < N) b[i] = max2(a[3 * i], a[3 * i + 1]);
+            else b[i] = a[3 * i];
+        }
+        return TreeMax<M>::of(b);
+    }
+};
+template <> struct TreeMax<1> {
+    static __device__ __forceinline__ float of(const float (&a)[1]) { return a[0]; }
+};
 
 // Key (row) position held by accumulator register r of a 32x32 MFMA output
 // in wave half hh: 8*(r/4) + 4*hh + r%4.
@@ -171,6 +215,7 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     constexpr int KT = D / 16;    // MFMA k-steps over d
     constexpr int DB = D / 32;    // 32-row blocks of O^T
     constexpr int PT = kBC / 16;  // MFMA k-steps over the keys of a tile
+    constexpr int NKB = kBC / 32; // 32-key blocks of S^T per tile
 
     __shared__ __attribute__((aligned(1024))) unsigned char k0s[T::kBytes];
     __shared__ __attribute__((aligned(1024))) unsigned char k1s[T::kBytes];
@@ -187,8 +232,7 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    // wave index as a scalar: every per-wave decision below is a scalar branch
-    const int w = (tid >> 6);
+    const int w = tid >> 6;       // wave index (kRowsPerWave query rows each)
     const int l32 = lane & 31;
     const int hh = lane >> 5;
 
@@ -222,25 +266,33 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         qf[kk] = __builtin_bit_cast(u16x8, x);
     }
 
-    const int n_keys_tiles = (N + kBC - 1) / kBC;
-    const int n_tiles = CAUSAL ? min(n_keys_tiles, (qblk + 1) * (kBR / kBC)) : n_keys_tiles;
+    const int n_keys_tiles = (N + kBC - 1) / kBC;      // compute steps over all keys
+    const int n_steps = CAUSAL ? min(n_keys_tiles, (qblk + 1) * (kBR / kBC)) : n_keys_tiles;
+    const int n_tiles = (n_steps + kNSub - 1) / kNSub; // LDS tiles of kLT keys
     // tiles this wave computes: causal rows q0..q0+31 need keys <= q0+31
-    const int n_w = (q0 >= N) ? 0 : (CAUSAL ? min(n_tiles, (q0 + kRowsPerWave - 1) / kBC + 1)
-                                            : n_tiles);
+    const int n_w = (q0 >= N) ? 0 : (CAUSAL ? min(n_steps, (q0 + kRowsPerWave - 1) / kBC + 1)
+                                            : n_steps);
 
     // ---- HBM -> LDS tile loads (each wave moves its share, 1 KB per load)
-    auto issue = [&](const __amdgpu_buffer_rsrc_t &r, auto buf, int t) {
-        constexpr bool is_v = decltype(buf)::value >= 2;
-#pragma unroll
-        for (int j = 0; j < T::kLoadsPerWave; ++j) {
-            const int li = w * T::kLoadsPerWave + j;
-            const int row = li * T::kRowsPerLoad + lane / T::kChunks;
-            const int pc = lane % T::kChunks;
-            const int lc = pc ^ (is_v ? T::vswz(row) : T::kswz(row));
-            const int off = (t * kBC + row) * T::kRowBytes + lc * 16;
+    // One of this wave's 1 KB loads of a tile: n < kLoadsPerWave is K, the
+    // rest V.  base = byte offset of the tile's first row; a base at or past
+    // 2^30 (>= every head's size) makes every lane out of range, which fills
+    // the LDS destination with zeros without touching memory.
+    static_assert(T::kLoads % kWaves == 0, "whole loads per wave");
+    auto issue_one = [&](int n, auto kbuf, auto vbuf, int base) {
+        const bool is_v = n >= T::kLoadsPerWave;
+        const int jn = is_v ? n - T::kLoadsPerWave : n;
+        const int li = jn * kWaves + w;
+        const int row = li * T::kRowsPerLoad + lane / T::kChunks;
+        const int pc = lane % T::kChunks;
+        const int lc = pc ^ (is_v ? T::vswz(row) : T::kswz(row));
+        const int off = base + row * T::kRowBytes + lc * 16;
+        if (is_v)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (LDS void *)(bufp(buf) + li * 1024), 16, off, 0, 0, 0);
-        }
+                rv, (LDS void *)(bufp(vbuf) + li * 1024), 16, off, 0, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rk, (LDS void *)(bufp(kbuf) + li * 1024), 16, off, 0, 0, 0);
     };
 
     // Per-lane LDS offsets of the MFMA operand reads (loop invariant).
@@ -259,49 +311,60 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         }
     }
 
+    int sub = 0;   // which kBC-key half of the LDS tile the current step uses
     auto kfrag = [&](auto buf, int kb, int kk) -> u16x8 {
-        return *(const LDS u16x8 *)(bufp(buf) + kb * 32 * T::kRowBytes + koff[kk]);
+        return *(const LDS u16x8 *)(bufp(buf) + (sub * kBC + kb * 32) * T::kRowBytes + koff[kk]);
     };
     auto vfrag = [&](auto buf, int db, int kk) -> u16x8 {
-        const LDS unsigned char *p = bufp(buf) + kk * 16 * T::kRowBytes + voff[db];
+        const LDS unsigned char *p = bufp(buf) + (sub * kBC + kk * 16) * T::kRowBytes + voff[db];
         const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4 *)p);
         const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (LDS s16x4 *)(p + 8 * T::kRowBytes));
         return __builtin_bit_cast(u16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 
-    // S^T(j) = K_j Q^T: s[kb], keys 32*kb.., query column l32.  Operands
-    // are read from LDS kDepth k-steps ahead of their MFMAs.
-    constexpr int kDepth = 2;
-    auto qk = [&](f32x16 (&s)[2], auto buf) {
-        u16x8 kf[kDepth + 1][2];
+    // S^T(j) = K_j Q^T: s[kb], keys 32*kb.., query column l32.  Operand
+    // i (k-step i / NKB, key block i % NKB) is read from LDS kQkAhead MFMAs
+    // before its MFMA; the schedule is pinned (one read per MFMA) so the
+    // compiler cannot pull the reads up against their uses.  With loads, this
+    // wave's share of the next tile's HBM -> LDS loads rides along, one load
+    // every NR / NLD MFMAs, instead of all waves queueing them at once.
+    auto qk = [&](f32x16 (&s)[NKB], auto buf, auto loads, auto kbuf, auto vbuf, int base) {
+        constexpr bool LD = decltype(loads)::value;
+        constexpr int NR = KT * NKB;
+        constexpr int AH = kQkAhead;
+        constexpr int NLD = 2 * T::kLoadsPerWave;
+        static_assert(NR % NLD == 0, "loads spread evenly over the MFMAs");
+        constexpr int ST = NR / NLD;
+        u16x8 kf[NR];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < kDepth; ++i) {
-            kf[i][0] = kfrag(buf, 0, i);
-            kf[i][1] = kfrag(buf, 1, i);
-        }
+        for (int i = 0; i < AH; ++i) kf[i] = kfrag(buf, i % NKB, i / NKB);
 #pragma unroll
-        for (int kk = 0; kk < KT; ++kk) {
-            if (kk + kDepth < KT) {
-                kf[(kk + kDepth) % (kDepth + 1)][0] = kfrag(buf, 0, kk + kDepth);
-                kf[(kk + kDepth) % (kDepth + 1)][1] = kfrag(buf, 1, kk + kDepth);
+        for (int i = 0; i < NR; ++i) {
+            if (i + AH < NR) kf[i + AH] = kfrag(buf, (i + AH) % NKB, (i + AH) / NKB);
+            const int kb = i % NKB, kk = i / NKB;
+            if (kk == 0) {
+                const f32x16 z = {};
+                s[kb] = E::mfma(kf[i], qf[kk], z);
+            } else {
+                s[kb] = E::mfma(kf[i], qf[kk], s[kb]);
             }
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const u16x8 a = kf[kk % (kDepth + 1)][kb];
-                if (kk == 0) {
-                    const f32x16 z = {};
-                    s[kb] = E::mfma(a, qf[kk], z);
-                } else {
-                    s[kb] = E::mfma(a, qf[kk], s[kb]);
-                }
-            }
+            if (LD && i % ST == 0) issue_one(i / ST, kbuf, vbuf, base);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);      // DS reads
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            if (i < NR - AH) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (LD && i % ST == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    auto mask = [&](f32x16 (&s)[2], int t) {
+    auto mask = [&](f32x16 (&s)[NKB], int t) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = t * kBC + 32 * kb + acc_row(r, hh);
@@ -320,20 +383,11 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
     // Row max of S(j) and the (lazy) update of the reference max.
-    auto update_max = [&](f32x16 (&s)[2]) {
-        // 32 values -> 11 -> 4 -> 1 with three-input maxima (depth 4)
-        float t1[11];
+    auto update_max = [&](f32x16 (&s)[NKB]) {
+        float v[NKB * 16];
 #pragma unroll
-        for (int i = 0; i < 10; ++i) {
-            const int a = 3 * i, b = 3 * i + 1, e = 3 * i + 2;
-            t1[i] = fmaxf(fmaxf(s[a >> 4][a & 15], s[b >> 4][b & 15]), s[e >> 4][e & 15]);
-        }
-        t1[10] = fmaxf(s[1][14], s[1][15]);
-        const float u0 = fmaxf(fmaxf(t1[0], t1[1]), t1[2]);
-        const float u1 = fmaxf(fmaxf(t1[3], t1[4]), t1[5]);
-        const float u2 = fmaxf(fmaxf(t1[6], t1[7]), t1[8]);
-        const float u3 = fmaxf(t1[9], t1[10]);
-        const float mx = fmaxf(fmaxf(fmaxf(u0, u1), u2), u3);
+        for (int i = 0; i < NKB * 16; ++i) v[i] = s[i >> 4][i & 15];
+        const float mx = TreeMax<NKB * 16>::of(v);
         const float mt = half_max(mx) * c;
         if (__builtin_amdgcn_ballot_w64(mt > m + kLazy)) {
             const float mn = fmaxf(m, mt);
@@ -355,13 +409,13 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     // cancels).  lse uses the fp32 sum for bfloat16; for binary16 the
     // rounded sum is within 2^-11 relative of it (|lse error| <= 4.9e-4),
     // so it serves for both.
-    auto softmax = [&](f32x16 (&s)[2], u32x4 (&pk)[PT]) {
+    auto softmax = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PT]) {
         const float mu = (m == neg_inf()) ? 0.f : m;
         float rs[4], rh[4];
         // groups of 8 scores: 8 FMAs, 8 exps, then sums and packing, so the
         // temporaries die inside the group (scheduling barrier per group)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < 2 * NKB; ++g) {
             const int kb = g >> 1, r0 = (g & 1) * 8;
             float x[8], p[8];
 #pragma unroll
@@ -384,20 +438,28 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         lh += (rh[0] + rh[1]) + (rh[2] + rh[3]);
     };
 
-    // O^T += V_j^T P(j)^T, operands prefetched 2*kDepth MFMAs ahead
+    // O^T += V_j^T P(j)^T, operand i (k-step i / DB, d block i % DB) read
+    // kPvAhead MFMAs ahead, schedule pinned as in qk (two reads per MFMA)
     auto pv = [&](auto buf, u32x4 (&pk)[PT]) {
-        constexpr int NM = PT * DB;        // MFMAs, index i -> kk = i / DB, db = i % DB
-        constexpr int AHEAD = 2 * kDepth;
-        u16x8 vf[AHEAD + 1];
+        constexpr int NM = PT * DB;
+        constexpr int AH = kPvAhead;
+        u16x8 vf[NM];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < AHEAD; ++i) vf[i] = vfrag(buf, i % DB, i / DB);
+        for (int i = 0; i < AH; ++i) vf[i] = vfrag(buf, i % DB, i / DB);
 #pragma unroll
         for (int i = 0; i < NM; ++i) {
-            if (i + AHEAD < NM)
-                vf[(i + AHEAD) % (AHEAD + 1)] = vfrag(buf, (i + AHEAD) % DB, (i + AHEAD) / DB);
-            oacc[i % DB] = E::mfma(vf[i % (AHEAD + 1)],
-                                   __builtin_bit_cast(u16x8, pk[i / DB]), oacc[i % DB]);
+            if (i + AH < NM) vf[i + AH] = vfrag(buf, (i + AH) % DB, (i + AH) / DB);
+            oacc[i % DB] = E::mfma(vf[i], __builtin_bit_cast(u16x8, pk[i / DB]), oacc[i % DB]);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);  // DS reads
+#pragma unroll
+        for (int i = 0; i < NM - AH; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     auto tile_masked = [&](int t) {
@@ -405,43 +467,44 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         return __builtin_amdgcn_readfirstlane((int)mk) != 0;
     };
 
-    // ---- prologue: K_0, V_0, K_1 in flight; S(0)
-    issue(rk, Buf<0>{}, 0);
-    issue(rv, Buf<2>{}, 0);
-    if (n_tiles > 1) issue(rk, Buf<1>{}, 1);
+    // ---- tile loop.  LDS tile t (kLT keys: K_t in k[t%2], V_t in v[t%2]) is
+    // computed as kNSub steps of kBC keys, j = kNSub*t + u, each
+    // QK^T(j) -> max -> softmax -> P(j).V.  Tile t+1 streams into the other
+    // buffers during step u = 0 (those were last read in tile t-1, before the
+    // barrier that ended it); waves that skip the step still issue their
+    // share.  After the last tile the loads are aimed out of range (zero
+    // fill of a buffer nobody reads, no memory traffic).
+#pragma unroll
+    for (int n = 0; n < 2 * T::kLoadsPerWave; ++n) issue_one(n, Buf<0>{}, Buf<2>{}, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    f32x16 sA[2], sB[2];
-    if (n_w > 0) {
-        qk(sA, Buf<0>{});
-        if (tile_masked(0)) mask(sA, 0);
-        update_max(sA);
-    }
-    __syncthreads();   // K_0 fully consumed before K_2 overwrites buffer 0
-
-    // One tile step (t has parity P): P(t) from scur, O += V_t P(t), then
-    // S(t+1) into snext; meanwhile K_{t+2} and V_{t+1} stream into the
-    // buffers that step t-1 finished with.
-    auto step = [&](auto par, int t, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+    f32x16 sc[NKB];
+    auto tile = [&](auto par, int t) {
         constexpr int P = decltype(par)::value;
-        if (t + 2 < n_tiles) issue(rk, Buf<P>{}, t + 2);
-        if (t + 1 < n_tiles) issue(rv, Buf<3 - P>{}, t + 1);
-        if (t < n_w) {
-            u32x4 pk[PT];
-            if (t + 1 < n_w) {
-                softmax(scur, pk);
+        const int base = (t + 1 < n_tiles) ? (t + 1) * kLT * T::kRowBytes : (1 << 30);
+#pragma unroll
+        for (int u = 0; u < kNSub; ++u) {
+            const int j = kNSub * t + u;
+            if (j < n_w) {
+                sub = u;
+                u32x4 pk[PT];
+                __builtin_amdgcn_s_setprio(2);
+                if (u == 0) qk(sc, Buf<P>{}, Flag<true>{}, Buf<1 - P>{}, Buf<3 - P>{}, base);
+                else qk(sc, Buf<P>{}, Flag<false>{}, Buf<1 - P>{}, Buf<3 - P>{}, base);
+                __builtin_amdgcn_s_setprio(0);
+                if (tile_masked(j)) mask(sc, j);
+                update_max(sc);
+                softmax(sc, pk);
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_setprio(2);
                 pv(Buf<2 + P>{}, pk);
-                __builtin_amdgcn_sched_barrier(0);
-                qk(snext, Buf<1 - P>{});
                 __builtin_amdgcn_s_setprio(0);
-                if (tile_masked(t + 1)) mask(snext, t + 1);
-                update_max(snext);
-            } else {
-                softmax(scur, pk);
-                pv(Buf<2 + P>{}, pk);
+                __builtin_amdgcn_sched_barrier(0);
+            } else if (u == 0) {
+#pragma unroll
+                for (int n = 0; n < 2 * T::kLoadsPerWave; ++n)
+                    issue_one(n, Buf<1 - P>{}, Buf<3 - P>{}, base);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);
@@ -449,8 +512,8 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     };
 
     for (int t = 0; t < n_tiles; t += 2) {
-        step(Buf<0>{}, t, sA, sB);
-        if (t + 1 < n_tiles) step(Buf<1>{}, t + 1, sB, sA);
+        tile(Buf<0>{}, t);
+        if (t + 1 < n_tiles) tile(Buf<1>{}, t + 1);
     }
 
     // ---- epilogue: one division per row, 16-bit O, fp32 lse
