@@ -24,6 +24,13 @@ Functions and what pins them (tests/test_oracle.py):
                   attn_fwd at several tile sizes
   softmax_1d / softmax_online_1d  [P-baidu] §4.1 / [P-wmrh] §2.1 -- library
                   softmax and each other
+  attn_bwd        gradients dQ, dK, dV of the plain definition for an upstream
+                  dO (chain rule; the pages print no gradient formulas) --
+                  torch fp64 autograd, central differences of a pure-Python
+                  forward, closed-form invariants (sum_j dK_j = 0,
+                  sum_j dV_j = sum_i dO_i, constant V, causal row 0)
+  attn_bwd_rows   the same on sampled query rows (dQ) and key rows (dK, dV)
+                  -- agreement with attn_bwd
   decode          binary16 / bfloat16 decoders -- all 65536 patterns vs a
                   library cast, hand-checked values
 """
@@ -75,8 +82,12 @@ def _bind(lib):
     lib.oracle_attn_probs.argtypes = [p, p, p, i32, i64, i64, i64, i64, i32, f64, p]
     lib.oracle_attn_fwd_tiled.argtypes = [p, p, p, i32, i64, i64, i64, i64, i32, f64,
                                           i64, i64, p, p]
+    lib.oracle_attn_bwd.argtypes = [p, p, p, p, i32, i64, i64, i64, i64, i32, f64, p, p, p]
+    lib.oracle_attn_bwd_rows.argtypes = [p, p, p, p, i32, i64, i64, i64, i64, i32, f64,
+                                         p, i64, p, i64, p, p, p]
     for name in ("oracle_decode", "oracle_num_threads", "oracle_attn_fwd",
-                 "oracle_attn_fwd_rows", "oracle_attn_probs", "oracle_attn_fwd_tiled"):
+                 "oracle_attn_fwd_rows", "oracle_attn_probs", "oracle_attn_fwd_tiled",
+                 "oracle_attn_bwd", "oracle_attn_bwd_rows"):
         getattr(lib, name).restype = ctypes.c_int
     lib.oracle_softmax_1d.restype = None
     lib.oracle_softmax_online_1d.restype = None
@@ -200,8 +211,44 @@ def _impl_attn_fwd_tiled(lib, q, k, v, dtype, causal: bool, scale: float,
     return o, lse
 
 
+def _impl_attn_bwd(lib, q, k, v, do, dtype, causal: bool, scale: float):
+    """Gradients of the exact attention for upstream gradient do, in fp64.
+    Returns (dq, dk, dv), each [B,H,N,d]."""
+    q, k, v, do = _bits(q), _bits(k), _bits(v), _bits(do)
+    B, H, N, d = _shape(q, k, v)
+    if do.shape != q.shape:
+        raise ValueError("do must have the [B,H,N,d] shape of q")
+    dq = np.empty((B, H, N, d), dtype=np.float64)
+    dk = np.empty_like(dq)
+    dv = np.empty_like(dq)
+    _check(lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _dtype_code(dtype),
+                               B, H, N, d, int(bool(causal)), float(scale),
+                               _ptr(dq), _ptr(dk), _ptr(dv)), "oracle_attn_bwd")
+    return dq, dk, dv
+
+
+def _impl_attn_bwd_rows(lib, q, k, v, do, dtype, causal: bool, scale: float,
+                        qrows, krows):
+    """dq on flat query rows qrows and (dk, dv) on flat key rows krows
+    ((b*H+h)*N+i).  Returns (dq [n_q,d], dk [n_k,d], dv [n_k,d])."""
+    q, k, v, do = _bits(q), _bits(k), _bits(v), _bits(do)
+    B, H, N, d = _shape(q, k, v)
+    if do.shape != q.shape:
+        raise ValueError("do must have the [B,H,N,d] shape of q")
+    qrows = np.ascontiguousarray(qrows, dtype=np.int64)
+    krows = np.ascontiguousarray(krows, dtype=np.int64)
+    dq = np.empty((qrows.size, d), dtype=np.float64)
+    dk = np.empty((krows.size, d), dtype=np.float64)
+    dv = np.empty((krows.size, d), dtype=np.float64)
+    _check(lib.oracle_attn_bwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _dtype_code(dtype),
+                                    B, H, N, d, int(bool(causal)), float(scale),
+                                    _ptr(qrows), qrows.size, _ptr(krows), krows.size,
+                                    _ptr(dq), _ptr(dk), _ptr(dv)), "oracle_attn_bwd_rows")
+    return dq, dk, dv
+
+
 _API = ("num_threads", "decode", "softmax_1d", "softmax_online_1d", "attn_fwd",
-        "attn_fwd_rows", "attn_probs", "attn_fwd_tiled")
+        "attn_fwd_rows", "attn_probs", "attn_fwd_tiled", "attn_bwd", "attn_bwd_rows")
 
 
 class Oracle:
@@ -238,3 +285,5 @@ attn_fwd = _module_fn("attn_fwd")
 attn_fwd_rows = _module_fn("attn_fwd_rows")
 attn_probs = _module_fn("attn_probs")
 attn_fwd_tiled = _module_fn("attn_fwd_tiled")
+attn_bwd = _module_fn("attn_bwd")
+attn_bwd_rows = _module_fn("attn_bwd_rows")

@@ -401,3 +401,218 @@ int oracle_attn_fwd_tiled(const uint16_t *q, const uint16_t *k,
     free_problem(&p);
     return 0;
 }
+
+/* ---- gradients of the plain definition ------------------------------------
+ *
+ * The pages state that the forward pass keeps the per-row statistics (the
+ * maximum and the denominator, here packed as lse) so that the backward pass
+ * can use them ([P-baidu] §6, "numerator and denominator kept apart", and the
+ * V1/V2 comparison of §7; [P-wmrh] §2.3 outputs l and m), but print no
+ * gradient formulas.  This is the gradient of the forward definition above,
+ * obtained by the chain rule, for an upstream gradient dO of O:
+ *
+ *   P_ij  = softmax_j(s_i)               (j in A_i, 0 elsewhere)
+ *   dV_j  = sum_i P_ij dO_i              (O = P V)
+ *   dP_ij = dO_i . v_j
+ *   dS_ij = P_ij (dP_ij - sum_t P_it dP_it)      (Jacobian of the softmax)
+ *   dQ_i  = scale * sum_j dS_ij k_j      (s_ij = scale q_i . k_j)
+ *   dK_j  = scale * sum_i dS_ij q_i
+ *
+ * fp64 throughout; dO is a 16-bit input like q, k, v.  All outputs fp64.
+ */
+
+typedef struct {
+    problem p;
+    double *dO;
+} bproblem;
+
+static int load_bproblem(bproblem *bp, const uint16_t *q, const uint16_t *k,
+                         const uint16_t *v, const uint16_t *dO, int dtype,
+                         int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                         double scale)
+{
+    int rc = load_problem(&bp->p, q, k, v, dtype, B, H, N, d, causal, scale);
+    if (rc) return rc;
+    int64_t n = B * H * N * d;
+    bp->dO = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    if (!bp->dO) { free_problem(&bp->p); return -2; }
+    decode_all(dO, dtype, n, bp->dO);
+    return 0;
+}
+
+static void free_bproblem(bproblem *bp)
+{
+    free_problem(&bp->p);
+    free(bp->dO);
+}
+
+/* Row i of head bh: P_i. (into prow, nkeys entries), dP_i. (into dprow) and
+ * returns D_i = sum_t P_it dP_it; *lse_out (if not NULL) = ln sum_t exp(s_it). */
+static double grad_row(const bproblem *bp, int64_t bh, int64_t i, double *prow,
+                       double *dprow, double *lse_out)
+{
+    const problem *p = &bp->p;
+    const int64_t N = p->N, d = p->d;
+    const double *qi = p->q + (bh * N + i) * d;
+    const double *doi = bp->dO + (bh * N + i) * d;
+    const double *kh = p->k + bh * N * d;
+    const double *vh = p->v + bh * N * d;
+    const int64_t nkeys = p->causal ? i + 1 : N;
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
+        prow[j] = p->scale * dot;
+        if (prow[j] > m) m = prow[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        prow[j] = exp(prow[j] - m);
+        l += prow[j];
+    }
+    if (lse_out) *lse_out = m + log(l);
+    double D = 0.0;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        prow[j] /= l;
+        double dp = 0.0;
+        for (int64_t c = 0; c < d; ++c) dp += doi[c] * vh[j * d + c];
+        dprow[j] = dp;
+        D += prow[j] * dp;
+    }
+    return D;
+}
+
+/* Full gradients: dq, dk, dv are [B,H,N,d] fp64.  Heads run in parallel;
+ * within a head the rows run in order (dk and dv sum over rows). */
+int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                    const uint16_t *dO, int dtype, int64_t B, int64_t H,
+                    int64_t N, int64_t d, int causal, double scale, double *dq,
+                    double *dk, double *dv)
+{
+    bproblem bp;
+    int rc = load_bproblem(&bp, q, k, v, dO, dtype, B, H, N, d, causal, scale);
+    if (rc) return rc;
+    const int64_t n = B * H * N * d;
+    for (int64_t t = 0; t < n; ++t) dq[t] = dk[t] = dv[t] = 0.0;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *prow = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        double *dprow = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (!prow || !dprow) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bh = 0; bh < B * H; ++bh) {
+                const double *qh = bp.p.q + bh * N * d, *kh = bp.p.k + bh * N * d;
+                const double *doh = bp.dO + bh * N * d;
+                double *dqh = dq + bh * N * d, *dkh = dk + bh * N * d, *dvh = dv + bh * N * d;
+                for (int64_t i = 0; i < N; ++i) {
+                    const double D = grad_row(&bp, bh, i, prow, dprow, NULL);
+                    const int64_t nkeys = causal ? i + 1 : N;
+                    for (int64_t j = 0; j < nkeys; ++j) {
+                        const double ds = prow[j] * (dprow[j] - D);
+                        for (int64_t c = 0; c < d; ++c) {
+                            dqh[i * d + c] += scale * ds * kh[j * d + c];
+                            dkh[j * d + c] += scale * ds * qh[i * d + c];
+                            dvh[j * d + c] += prow[j] * doh[i * d + c];
+                        }
+                    }
+                }
+            }
+        }
+        free(prow);
+        free(dprow);
+    }
+    free_bproblem(&bp);
+    return fail ? -2 : 0;
+}
+
+/* Sampled gradients for inputs too large for oracle_attn_bwd: dq for the
+ * flat query rows qrows[] ((b*H+h)*N+i) and dk, dv for the flat key rows
+ * krows[] ((b*H+h)*N+j); outputs packed [n_q,d] and [n_k,d].  A key row
+ * needs P_ij and D_i of every query row of its head, so those heads' rows
+ * are evaluated once first (lse_i and D_i kept per row). */
+int oracle_attn_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         const uint16_t *dO, int dtype, int64_t B, int64_t H,
+                         int64_t N, int64_t d, int causal, double scale,
+                         const int64_t *qrows, int64_t n_q, const int64_t *krows,
+                         int64_t n_k, double *dq_rows, double *dk_rows,
+                         double *dv_rows)
+{
+    const int64_t total = B * H * N;
+    for (int64_t t = 0; t < n_q; ++t)
+        if (qrows[t] < 0 || qrows[t] >= total) return -1;
+    for (int64_t t = 0; t < n_k; ++t)
+        if (krows[t] < 0 || krows[t] >= total) return -1;
+    bproblem bp;
+    int rc = load_bproblem(&bp, q, k, v, dO, dtype, B, H, N, d, causal, scale);
+    if (rc) return rc;
+    int fail = 0;
+    /* per-row D_i of every head that a sampled key belongs to */
+    char *need = (char *)calloc((size_t)(B * H > 0 ? B * H : 1), 1);
+    double *Dall = (double *)malloc((size_t)(total > 0 ? total : 1) * sizeof(double));
+    double *Lall = (double *)malloc((size_t)(total > 0 ? total : 1) * sizeof(double));
+    if (!need || !Dall || !Lall) {
+        free(need); free(Dall); free(Lall); free_bproblem(&bp);
+        return -2;
+    }
+    for (int64_t t = 0; t < n_k; ++t) need[krows[t] / N] = 1;
+#pragma omp parallel
+    {
+        double *prow = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        double *dprow = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (!prow || !dprow) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < total; ++r)
+                if (need[r / N]) Dall[r] = grad_row(&bp, r / N, r % N, prow, dprow, Lall + r);
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t t = 0; t < n_q; ++t) {
+                const int64_t bh = qrows[t] / N, i = qrows[t] % N;
+                const double D = grad_row(&bp, bh, i, prow, dprow, NULL);
+                const int64_t nkeys = causal ? i + 1 : N;
+                const double *kh = bp.p.k + bh * N * d;
+                double *out = dq_rows + t * d;
+                for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
+                for (int64_t j = 0; j < nkeys; ++j) {
+                    const double ds = prow[j] * (dprow[j] - D);
+                    for (int64_t c = 0; c < d; ++c) out[c] += scale * ds * kh[j * d + c];
+                }
+            }
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t t = 0; t < n_k; ++t) {
+                const int64_t bh = krows[t] / N, j = krows[t] % N;
+                double *ok = dk_rows + t * d, *ov = dv_rows + t * d;
+                for (int64_t c = 0; c < d; ++c) ok[c] = ov[c] = 0.0;
+                const double *kj = bp.p.k + (bh * N + j) * d;
+                const double *vj = bp.p.v + (bh * N + j) * d;
+                for (int64_t i = causal ? j : 0; i < N; ++i) {
+                    const double *qi = bp.p.q + (bh * N + i) * d;
+                    const double *doi = bp.dO + (bh * N + i) * d;
+                    double dot = 0.0, dp = 0.0;
+                    for (int64_t c = 0; c < d; ++c) {
+                        dot += qi[c] * kj[c];
+                        dp += doi[c] * vj[c];
+                    }
+                    const double pij = exp(scale * dot - Lall[bh * N + i]);
+                    const double ds = pij * (dp - Dall[bh * N + i]);
+                    for (int64_t c = 0; c < d; ++c) {
+                        ok[c] += scale * ds * qi[c];
+                        ov[c] += pij * doi[c];
+                    }
+                }
+            }
+        }
+        free(prow);
+        free(dprow);
+    }
+    free(need);
+    free(Dall);
+    free(Lall);
+    free_bproblem(&bp);
+    return fail ? -2 : 0;
+}

@@ -173,6 +173,98 @@ def pin_rows(orc) -> bool:
     return ok
 
 
+# ---------------------------------------------------------------- gradients
+
+def torch_grad_reference(q, k, v, do, causal: bool, scale: float):
+    """dQ, dK, dV by torch fp64 autograd through the library attention of
+    torch_reference (inputs decoded by torch's own cast)."""
+    qq, kk, vv = (t.double().clone().requires_grad_() for t in (q, k, v))
+    s = torch.matmul(qq, kk.transpose(-1, -2)) * float(scale)
+    N = q.shape[-2]
+    if causal:
+        s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    o = torch.matmul(torch.softmax(s, dim=-1), vv)
+    o.backward(do.double())
+    return qq.grad.numpy(), kk.grad.numpy(), vv.grad.numpy()
+
+
+def _loss_python(q64, k64, v64, do64, causal, scale) -> float:
+    """sum(dO * O) with O from the pure-Python forward (fp64 inputs)."""
+    o, _ = python_reference(q64, k64, v64, causal, scale)
+    return math.fsum((o * do64.numpy()).ravel().tolist())
+
+
+def pin_bwd_autograd(orc) -> bool:
+    ok = True
+    for dtype in ("f16", "bf16"):
+        for causal in (False, True):
+            for (B, H, N, d) in ((1, 2, 13, 8), (2, 1, 5, 3)):
+                q, k, v = _qkv(B, H, N, d, dtype, seed=N + d)
+                do = _qkv(B, H, N, d, dtype, seed=N + d + 100)[0]
+                dq, dk, dv = orc.attn_bwd(bits(q), bits(k), bits(v), bits(do), dtype, causal, 0.4)
+                rq, rk, rv = torch_grad_reference(q, k, v, do, causal, 0.4)
+                ok &= _close(dq, rq, 1e-12) and _close(dk, rk, 1e-12) and _close(dv, rv, 1e-12)
+    return ok
+
+
+def pin_bwd_finite_difference(orc) -> bool:
+    """Central differences of sum(dO * O), O from the pure-Python loops:
+    d/dx_e = (L(x + h e) - L(x - h e)) / 2h, for every element of q, k, v."""
+    q, k, v = _qkv(1, 1, 4, 3, "f16", seed=12)
+    do = _qkv(1, 1, 4, 3, "f16", seed=13)[0]
+    h = 1e-6
+    ok = True
+    for causal in (False, True):
+        dq, dk, dv = orc.attn_bwd(bits(q), bits(k), bits(v), bits(do), "f16", causal, 0.6)
+        base = [q.double(), k.double(), v.double()]
+        for which, got in enumerate((dq, dk, dv)):
+            fd = np.zeros(got.shape)
+            for idx in np.ndindex(*got.shape):
+                plus = [t.clone() for t in base]
+                minus = [t.clone() for t in base]
+                plus[which][idx] += h
+                minus[which][idx] -= h
+                fd[idx] = (_loss_python(*plus, do.double(), causal, 0.6)
+                           - _loss_python(*minus, do.double(), causal, 0.6)) / (2 * h)
+            ok &= _close(got, fd, 1e-7)
+    return ok
+
+
+def pin_bwd_invariants(orc) -> bool:
+    """sum_j dK_j = 0 (every row of dS sums to zero), sum_j dV_j = sum_i dO_i
+    (every row of P sums to one), constant V gives dQ = dK = 0, and causal
+    row 0 (one key, weight 1) gets dQ_0 = 0."""
+    ok = True
+    for causal in (False, True):
+        q, k, v = _qkv(2, 2, 21, 16, "bf16", seed=14)
+        do = _qkv(2, 2, 21, 16, "bf16", seed=15)[0]
+        dq, dk, dv = orc.attn_bwd(bits(q), bits(k), bits(v), bits(do), "bf16", causal, 0.3)
+        ok &= _close(dk.sum(2), np.zeros((2, 2, 16)), 1e-12)
+        ok &= _close(dv.sum(2), do.double().numpy().sum(2), 1e-12)
+        if causal:
+            ok &= _close(dq[:, :, 0, :], np.zeros((2, 2, 16)), 1e-15)
+        vc = v[:, :, :1, :].expand(2, 2, 21, 16).contiguous()
+        dq2, dk2, _ = orc.attn_bwd(bits(q), bits(k), bits(vc), bits(do), "bf16", causal, 0.3)
+        ok &= _close(dq2, np.zeros_like(dq2), 1e-13) and _close(dk2, np.zeros_like(dk2), 1e-13)
+    return ok
+
+
+def pin_bwd_rows(orc) -> bool:
+    q, k, v = _qkv(2, 2, 19, 8, "f16", seed=16)
+    do = _qkv(2, 2, 19, 8, "f16", seed=17)[0]
+    qr = np.array([0, 4, 18, 19, 40, 75], dtype=np.int64)
+    kr = np.array([0, 1, 18, 20, 37, 75], dtype=np.int64)
+    ok = True
+    for causal in (False, True):
+        dq, dk, dv = orc.attn_bwd(bits(q), bits(k), bits(v), bits(do), "f16", causal, 0.35)
+        a, b, c = orc.attn_bwd_rows(bits(q), bits(k), bits(v), bits(do), "f16", causal, 0.35,
+                                    qr, kr)
+        ok &= _close(a, dq.reshape(-1, 8)[qr], 1e-12)
+        ok &= _close(b, dk.reshape(-1, 8)[kr], 1e-12)
+        ok &= _close(c, dv.reshape(-1, 8)[kr], 1e-12)
+    return ok
+
+
 PINS = {
     "brute_force": pin_brute_force,
     "python_loops": pin_python_loops,
@@ -183,6 +275,10 @@ PINS = {
     "causal_row0": pin_causal_row0,
     "probs": pin_probs,
     "rows": pin_rows,
+    "bwd_autograd": pin_bwd_autograd,
+    "bwd_finite_difference": pin_bwd_finite_difference,
+    "bwd_invariants": pin_bwd_invariants,
+    "bwd_rows": pin_bwd_rows,
 }
 
 

@@ -287,13 +287,18 @@ def test_tiny_workload_against_library(oracle_mod):
 MUTANTS = [
     ("s[j] = p->scale * dot;", "s[j] = dot;", "dropped scale"),
     ("double w = exp(s[j] - m);", "double w = exp(m - s[j]);", "sign of the exponent"),
-    ("p->causal ? i + 1 : N;", "p->causal ? i : N;", "causal off by one"),
-    ("p->causal ? i + 1 : N;", "p->causal ? N : N;", "causal mask dropped"),
+    ("p->causal ? i + 1 : N;     /* |A_i| */", "p->causal ? i : N;", "causal off by one"),
+    ("p->causal ? i + 1 : N;     /* |A_i| */", "p->causal ? N : N;", "causal mask dropped"),
     ("for (int64_t c = 0; c < d; ++c) o_out[c] /= l;", "", "normalisation dropped"),
-    ("*lse_out = m + log(l);", "*lse_out = log(l);", "lse without the max"),
+    ("\n    *lse_out = m + log(l);", "\n    *lse_out = log(l);", "lse without the max"),
+    ("if (lse_out) *lse_out = m + log(l);", "if (lse_out) *lse_out = log(l);",
+     "bwd rows: row lse without the max"),
     ("o_out[c] += w * vh[j * d + c];", "o_out[c] += w * vh[i * d + c];", "V row index"),
-    ("dot += qi[c] * kh[j * d + c];", "dot += qi[c] * kh[j * d + (d - 1 - c)];",
+    ("dot += qi[c] * kh[j * d + c];\n        s[j]", "dot += qi[c] * kh[j * d + (d - 1 - c)];\n        s[j]",
      "feature index of K reversed"),
+    ("dot += qi[c] * kh[j * d + c];\n        prow[j]",
+     "dot += qi[c] * kh[j * d + (d - 1 - c)];\n        prow[j]",
+     "bwd: feature index of K reversed in the row weights"),
     ("if (s[j] > m) m = s[j];", "m = 0.0;", "no max subtraction"),
     ("ldexp((double)(1024 + f), e - 25)", "ldexp((double)(1024 + f), e - 24)",
      "binary16 exponent bias"),
@@ -310,7 +315,71 @@ MUTANTS = [
      "online 1-D: sum not rescaled"),
     ("for (int64_t j = 0; j < n; ++j) l += exp(x[j] - m);",
      "for (int64_t j = 1; j < n; ++j) l += exp(x[j] - m);", "1-D: first term dropped"),
+    # gradients
+    ("const double ds = prow[j] * (dprow[j] - D);\n                        for",
+     "const double ds = prow[j] * dprow[j];\n                        for",
+     "bwd: softmax Jacobian without the row term"),
+    ("dqh[i * d + c] += scale * ds * kh[j * d + c];", "dqh[i * d + c] += ds * kh[j * d + c];",
+     "bwd: dQ without scale"),
+    ("dkh[j * d + c] += scale * ds * qh[i * d + c];",
+     "dkh[j * d + c] += scale * ds * kh[i * d + c];", "bwd: dK from K instead of Q"),
+    ("dvh[j * d + c] += prow[j] * doh[i * d + c];", "dvh[j * d + c] += prow[j] * doh[j * d + c];",
+     "bwd: dV row index"),
+    ("D += prow[j] * dp;", "D += dp;", "bwd: row term without P"),
+    ("const int64_t nkeys = p->causal ? i + 1 : N;\n    double m = -INFINITY;",
+     "const int64_t nkeys = p->causal ? N : N;\n    double m = -INFINITY;",
+     "bwd: causal mask dropped in the row weights"),
+    ("dp += doi[c] * vh[j * d + c];", "dp += doi[c] * vh[i * d + c];", "bwd: dP row index of V"),
+    ("const double ds = pij * (dp - Dall[bh * N + i]);",
+     "const double ds = pij * (Dall[bh * N + i] - dp);", "bwd rows: sign of dS"),
+    ("for (int64_t i = causal ? j : 0; i < N; ++i) {",
+     "for (int64_t i = causal ? j + 1 : 0; i < N; ++i) {", "bwd rows: causal diagonal dropped"),
+    ("const double pij = exp(scale * dot - Lall[bh * N + i]);",
+     "const double pij = exp(scale * dot);", "bwd rows: P without lse"),
+    ("out[c] += scale * ds * kh[j * d + c];", "out[c] += ds * kh[j * d + c];",
+     "bwd rows: dQ without scale"),
 ]
+
+
+# ---------------------------------------------------------------- gradients
+
+@pytest.mark.parametrize("name", ["bwd_autograd", "bwd_finite_difference", "bwd_invariants",
+                                  "bwd_rows"])
+def test_bwd_pin(oracle_mod, name):
+    assert PINS[name](oracle_mod)
+
+
+@pytest.mark.parametrize("N", [1, 2, 7, 33])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("scale", [0.0, -0.5, 0.125])
+def test_bwd_autograd_shapes(oracle_mod, N, causal, scale):
+    from tests.oracle_pins import torch_grad_reference
+    for dtype in ("f16", "bf16"):
+        q, k, v = make_qkv(1, 2, N, 8, dtype, seed=N * 7 + 1)
+        do = make_qkv(1, 2, N, 8, dtype, seed=N * 7 + 2)[0]
+        dq, dk, dv = oracle_mod.attn_bwd(bits(q), bits(k), bits(v), bits(do), dtype, causal, scale)
+        rq, rk, rv = torch_grad_reference(q, k, v, do, causal, scale)
+        for a, b in ((dq, rq), (dk, rk), (dv, rv)):
+            np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_bwd_two_key_closed_form(oracle_mod):
+    """N=2, d=1, non-causal: with t = s0 - s1 and w = sigmoid(t), o = v1 +
+    w (v0 - v1), so dO/dt = w(1-w)(v0 - v1) and dq_i = scale * dO_i * w(1-w)
+    (v0 - v1)(k0 - k1); dv_0 = sum_i dO_i w_i."""
+    qv = np.array([1.25, -0.5]); kv = np.array([0.75, -1.5]); vv = np.array([2.0, -3.0])
+    dov = np.array([0.5, -1.25])
+    q = to_tensor(qv.reshape(1, 1, 2, 1), "f16"); k = to_tensor(kv.reshape(1, 1, 2, 1), "f16")
+    v = to_tensor(vv.reshape(1, 1, 2, 1), "f16"); do = to_tensor(dov.reshape(1, 1, 2, 1), "f16")
+    scale = 0.625
+    dq, dk, dv = oracle_mod.attn_bwd(bits(q), bits(k), bits(v), bits(do), "f16", False, scale)
+    sig = lambda x: 1.0 / (1.0 + math.exp(-x))
+    w = [sig(scale * qv[i] * (kv[0] - kv[1])) for i in range(2)]
+    for i in range(2):
+        want = scale * dov[i] * w[i] * (1 - w[i]) * (vv[0] - vv[1]) * (kv[0] - kv[1])
+        assert dq[0, 0, i, 0] == pytest.approx(want, abs=1e-15)
+    assert dv[0, 0, 0, 0] == pytest.approx(dov[0] * w[0] + dov[1] * w[1], abs=1e-15)
+    assert dv[0, 0, 1, 0] == pytest.approx(dov[0] * (1 - w[0]) + dov[1] * (1 - w[1]), abs=1e-15)
 
 
 @pytest.fixture(scope="module")
