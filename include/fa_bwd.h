@@ -1,0 +1,70 @@
+/*
+ * fa_bwd.h -- C ABI of the MI355X (gfx950) exact-attention backward pass.
+ *
+ * Operation.  For the forward o = Softmax(scale * q k^T) v of fa_fwd.h and
+ * an upstream gradient dO of o, per batch b and head h:
+ *     P_ij  = exp(scale * q_i . k_j - lse_i)        (j allowed for i, else 0)
+ *     dV_j  = sum_i P_ij dO_i
+ *     dS_ij = P_ij (dO_i . v_j - D_i),   D_i = dO_i . o_i
+ *     dQ_i  = scale * sum_j dS_ij k_j
+ *     dK_j  = scale * sum_i dS_ij q_i
+ * with the allowed keys of fa_fwd (all, or j <= i when causal).  This is the
+ * chain rule through Attention(Q,K,V) = Softmax(Q K^T / sqrt(d)) V of
+ * "FlashAttention 优化原理与实现要点解析" (cloud.baidu.com) §1; the per-row
+ * statistics that page keeps apart for the backward pass (§6, numerator and
+ * denominator) arrive here as lse, the fp32 logsumexp fa_fwd writes, so P is
+ * recomputed tile by tile and never stored.  D_i = dO_i . o_i equals
+ * sum_j P_ij (dO_i . v_j) because o_i = sum_j P_ij v_j.
+ *
+ * Layout.  q, k, v, o, dO, dq, dk, dv are contiguous [B,H,N,d] arrays of one
+ * 16-bit type (binary16 or bfloat16), element (b,h,n,c) at
+ * ((b*H+h)*N+n)*d+c; lse is fp32 [B,H,N].  Accumulation is fp32; P and dS
+ * are rounded to the input type (nearest-even) as MFMA operands; dq, dk, dv
+ * are rounded to the input type once, at the end.
+ *
+ * Ownership.  All pointers are device pointers owned by the caller.  ws is a
+ * caller-owned fp32 workspace of fa_bwd_workspace_size(B, H, N) bytes; the
+ * call overwrites it (its contents afterwards are unspecified).  The library
+ * allocates nothing and keeps no state between calls.  q, k, v, o, dO and lse
+ * are only read; dq, dk and dv are fully overwritten.  No output or ws may
+ * overlap an input or another output.
+ *
+ * Errors.  As fa_fwd: arguments are validated on the host before any HIP
+ * call, and a failing call touches no memory.  A passing call enqueues three
+ * kernels on `stream` and returns without waiting.  Results are
+ * deterministic (no atomics): the same inputs give the same bits.
+ */
+#ifndef FA_BWD_H
+#define FA_BWD_H
+
+#include <stddef.h>
+#include "fa_fwd.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Bytes of fp32 workspace fa_bwd needs for B*H heads of N rows (0 if the
+ * sizes are not positive). */
+size_t fa_bwd_workspace_size(int B, int H, int N);
+
+/* Backward pass:
+ *   q, k, v, o, dO  [B,H,N,d] 16-bit (o and lse as written by fa_fwd for the
+ *                   same q, k, v, causal and scale), read only
+ *   lse             [B,H,N] fp32 (natural log), read only
+ *   ws              fa_bwd_workspace_size(B,H,N) bytes, 16-byte aligned,
+ *                   scratch
+ *   dq, dk, dv      [B,H,N,d] 16-bit, written
+ *   B, H, N, d, causal, scale, dtype: as fa_fwd (d 64 or 128)
+ * Returns FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED / FA_ERR_MISALIGNED /
+ * FA_ERR_LAUNCH under the same rules as fa_fwd (ws must be 16-byte aligned). */
+fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o,
+                 const void *dO, const float *lse, float *ws, void *dq, void *dk,
+                 void *dv, int B, int H, int N, int d, int causal, float scale,
+                 fa_dtype dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_BWD_H */

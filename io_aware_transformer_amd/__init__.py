@@ -1,14 +1,18 @@
-"""Python binding of the MI355X exact-attention forward library (libfa_fwd.so).
+"""Python binding of the MI355X exact-attention library (libfa_fwd.so).
 
-Argument marshalling only: every step of the forward pass runs in the HIP
-kernels behind the C ABI declared in include/fa_fwd.h.  PyTorch supplies
-device memory and streams.  There is no fallback: if the library cannot be
-loaded (or built with hipcc), every call raises.
+Argument marshalling only: every step of the forward and backward passes
+runs in the HIP kernels behind the C ABI declared in include/fa_fwd.h and
+include/fa_bwd.h.  PyTorch supplies device memory and streams.  There is no
+fallback: if the library cannot be loaded (or built with hipcc), every call
+raises.
 
 C entry points mirrored here with the same names and argument order:
   fa_fwd_f16(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> status
   fa_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> status
   fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream) -> status
+  fa_bwd(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale,
+         dtype, stream) -> status
+  fa_bwd_workspace_size(B, H, N) -> bytes
   fa_status_string(status) -> str
 Pointers may be given as integers or as tensors (their data_ptr()); the
 stream as an integer handle, a torch.cuda.Stream, or None (null stream).
@@ -28,7 +32,8 @@ FA_ERR_LAUNCH = -4
 FA_DTYPE_F16 = 0
 FA_DTYPE_BF16 = 1
 
-EXPORTED = ("fa_fwd_f16", "fa_fwd_bf16", "fa_fwd", "fa_status_string")
+EXPORTED = ("fa_fwd_f16", "fa_fwd_bf16", "fa_fwd", "fa_status_string", "fa_bwd",
+            "fa_bwd_workspace_size")
 
 _lib = None
 
@@ -62,6 +67,10 @@ def load():
         getattr(lib, n).restype = ctypes.c_int
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_bwd.argtypes = [p] * 10 + [i, i, i, i, i, f, i, p]
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i]
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -98,6 +107,17 @@ def fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream=None) -> in
                          _stream(stream))
 
 
+def fa_bwd(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale, dtype,
+           stream=None) -> int:
+    return load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(ws),
+                         _ptr(dq), _ptr(dk), _ptr(dv), int(B), int(H), int(N), int(d),
+                         int(causal), float(scale), int(dtype), _stream(stream))
+
+
+def fa_bwd_workspace_size(B, H, N) -> int:
+    return int(load().fa_bwd_workspace_size(int(B), int(H), int(N)))
+
+
 def fa_status_string(status: int) -> str:
     return load().fa_status_string(int(status)).decode()
 
@@ -130,3 +150,28 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, stream=
     if st != FA_OK:
         raise FaError(st)
     return o, lse
+
+
+def attention_backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
+                       stream=None):
+    """Gradients (dq, dk, dv) of attention(q, k, v) for upstream gradient do,
+    given the forward's o and lse.  Allocates the outputs and the workspace;
+    raises FaError on a non-zero status."""
+    import torch
+    dt = FA_DTYPE_F16 if q.dtype == torch.float16 else FA_DTYPE_BF16
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("q, k, v must be float16 or bfloat16")
+    for t in (k, v, o, do):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("k, v, o, do must be contiguous and match q")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa_bwd_workspace_size(B, H, N) // 4, dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_bwd(q, k, v, o, do, lse, ws, dq, dk, dv, B, H, N, d, int(causal), scale, dt, stream)
+    if st != FA_OK:
+        raise FaError(st)
+    return dq, dk, dv

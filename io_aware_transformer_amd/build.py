@@ -1,4 +1,5 @@
-"""Build the HIP library libfa_fwd.so in-tree for gfx950 with hipcc."""
+"""Build the HIP library libfa_fwd.so (forward and backward kernels) in-tree for
+gfx950 with hipcc."""
 from __future__ import annotations
 
 import os
@@ -8,8 +9,8 @@ from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
-SOURCES = [PKG / "csrc" / "fa_fwd.hip"]
-HEADERS = [ROOT / "include" / "fa_fwd.h"]
+SOURCES = [PKG / "csrc" / "fa_fwd.hip", PKG / "csrc" / "fa_bwd.hip"]
+HEADERS = [ROOT / "include" / "fa_fwd.h", ROOT / "include" / "fa_bwd.h"]
 LIB = PKG / "libfa_fwd.so"
 
 HIPCC_FLAGS = [

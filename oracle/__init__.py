@@ -29,6 +29,10 @@ Functions and what pins them (tests/test_oracle.py):
                   torch fp64 autograd, central differences of a pure-Python
                   forward, closed-form invariants (sum_j dK_j = 0,
                   sum_j dV_j = sum_i dO_i, constant V, causal row 0)
+                  With a given 16-bit o the row term is dO . o (as a backward
+                  pass fed the forward's output computes it) -- pinned by the
+                  exact linear shift it causes (dq by -scale dD (P K), dk by
+                  -scale P^T (dD q), dv unchanged)
   attn_bwd_rows   the same on sampled query rows (dQ) and key rows (dK, dV)
                   -- agreement with attn_bwd
   decode          binary16 / bfloat16 decoders -- all 65536 patterns vs a
@@ -82,8 +86,8 @@ def _bind(lib):
     lib.oracle_attn_probs.argtypes = [p, p, p, i32, i64, i64, i64, i64, i32, f64, p]
     lib.oracle_attn_fwd_tiled.argtypes = [p, p, p, i32, i64, i64, i64, i64, i32, f64,
                                           i64, i64, p, p]
-    lib.oracle_attn_bwd.argtypes = [p, p, p, p, i32, i64, i64, i64, i64, i32, f64, p, p, p]
-    lib.oracle_attn_bwd_rows.argtypes = [p, p, p, p, i32, i64, i64, i64, i64, i32, f64,
+    lib.oracle_attn_bwd.argtypes = [p, p, p, p, p, i32, i64, i64, i64, i64, i32, f64, p, p, p]
+    lib.oracle_attn_bwd_rows.argtypes = [p, p, p, p, p, i32, i64, i64, i64, i64, i32, f64,
                                          p, i64, p, i64, p, p, p]
     for name in ("oracle_decode", "oracle_num_threads", "oracle_attn_fwd",
                  "oracle_attn_fwd_rows", "oracle_attn_probs", "oracle_attn_fwd_tiled",
@@ -211,36 +215,51 @@ def _impl_attn_fwd_tiled(lib, q, k, v, dtype, causal: bool, scale: float,
     return o, lse
 
 
-def _impl_attn_bwd(lib, q, k, v, do, dtype, causal: bool, scale: float):
+def _given_o(o, shape):
+    if o is None:
+        return None
+    o = _bits(o)
+    if o.shape != shape:
+        raise ValueError("o must have the [B,H,N,d] shape of q")
+    return o
+
+
+def _impl_attn_bwd(lib, q, k, v, do, dtype, causal: bool, scale: float, o=None):
     """Gradients of the exact attention for upstream gradient do, in fp64.
+    With o (16-bit bits of a forward output) the row term is dO_i . o_i.
     Returns (dq, dk, dv), each [B,H,N,d]."""
     q, k, v, do = _bits(q), _bits(k), _bits(v), _bits(do)
     B, H, N, d = _shape(q, k, v)
     if do.shape != q.shape:
         raise ValueError("do must have the [B,H,N,d] shape of q")
+    o = _given_o(o, q.shape)
     dq = np.empty((B, H, N, d), dtype=np.float64)
     dk = np.empty_like(dq)
     dv = np.empty_like(dq)
-    _check(lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _dtype_code(dtype),
+    _check(lib.oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do),
+                               None if o is None else _ptr(o), _dtype_code(dtype),
                                B, H, N, d, int(bool(causal)), float(scale),
                                _ptr(dq), _ptr(dk), _ptr(dv)), "oracle_attn_bwd")
     return dq, dk, dv
 
 
 def _impl_attn_bwd_rows(lib, q, k, v, do, dtype, causal: bool, scale: float,
-                        qrows, krows):
+                        qrows, krows, o=None):
     """dq on flat query rows qrows and (dk, dv) on flat key rows krows
-    ((b*H+h)*N+i).  Returns (dq [n_q,d], dk [n_k,d], dv [n_k,d])."""
+    ((b*H+h)*N+i), optionally with the row term from a given o.
+    Returns (dq [n_q,d], dk [n_k,d], dv [n_k,d])."""
     q, k, v, do = _bits(q), _bits(k), _bits(v), _bits(do)
     B, H, N, d = _shape(q, k, v)
     if do.shape != q.shape:
         raise ValueError("do must have the [B,H,N,d] shape of q")
+    o = _given_o(o, q.shape)
     qrows = np.ascontiguousarray(qrows, dtype=np.int64)
     krows = np.ascontiguousarray(krows, dtype=np.int64)
     dq = np.empty((qrows.size, d), dtype=np.float64)
     dk = np.empty((krows.size, d), dtype=np.float64)
     dv = np.empty((krows.size, d), dtype=np.float64)
-    _check(lib.oracle_attn_bwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _dtype_code(dtype),
+    _check(lib.oracle_attn_bwd_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(do),
+                                    None if o is None else _ptr(o), _dtype_code(dtype),
                                     B, H, N, d, int(bool(causal)), float(scale),
                                     _ptr(qrows), qrows.size, _ptr(krows), krows.size,
                                     _ptr(dq), _ptr(dk), _ptr(dv)), "oracle_attn_bwd_rows")

@@ -419,24 +419,36 @@ int oracle_attn_fwd_tiled(const uint16_t *q, const uint16_t *k,
  *   dK_j  = scale * sum_i dS_ij q_i
  *
  * fp64 throughout; dO is a 16-bit input like q, k, v.  All outputs fp64.
+ *
+ * The row term sum_t P_it dP_it equals dO_i . O_i, because O_i =
+ * sum_t P_it v_t.  A backward pass that is handed the forward's 16-bit
+ * output o uses D_i = dO_i . o_i instead; passing o (16-bit bits, or NULL)
+ * selects that form, which differs from the plain one only through the
+ * rounding of o.
  */
 
 typedef struct {
     problem p;
     double *dO;
+    double *o;          /* decoded given output, or NULL */
 } bproblem;
 
 static int load_bproblem(bproblem *bp, const uint16_t *q, const uint16_t *k,
-                         const uint16_t *v, const uint16_t *dO, int dtype,
-                         int64_t B, int64_t H, int64_t N, int64_t d, int causal,
-                         double scale)
+                         const uint16_t *v, const uint16_t *dO, const uint16_t *o,
+                         int dtype, int64_t B, int64_t H, int64_t N, int64_t d,
+                         int causal, double scale)
 {
     int rc = load_problem(&bp->p, q, k, v, dtype, B, H, N, d, causal, scale);
     if (rc) return rc;
     int64_t n = B * H * N * d;
     bp->dO = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
-    if (!bp->dO) { free_problem(&bp->p); return -2; }
+    bp->o = o ? (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double)) : NULL;
+    if (!bp->dO || (o && !bp->o)) {
+        free(bp->dO); free(bp->o); free_problem(&bp->p);
+        return -2;
+    }
     decode_all(dO, dtype, n, bp->dO);
+    if (o) decode_all(o, dtype, n, bp->o);
     return 0;
 }
 
@@ -444,10 +456,12 @@ static void free_bproblem(bproblem *bp)
 {
     free_problem(&bp->p);
     free(bp->dO);
+    free(bp->o);
 }
 
 /* Row i of head bh: P_i. (into prow, nkeys entries), dP_i. (into dprow) and
- * returns D_i = sum_t P_it dP_it; *lse_out (if not NULL) = ln sum_t exp(s_it). */
+ * returns D_i = sum_t P_it dP_it (or dO_i . o_i when o is given);
+ * *lse_out (if not NULL) = ln sum_t exp(s_it). */
 static double grad_row(const bproblem *bp, int64_t bh, int64_t i, double *prow,
                        double *dprow, double *lse_out)
 {
@@ -479,18 +493,23 @@ static double grad_row(const bproblem *bp, int64_t bh, int64_t i, double *prow,
         dprow[j] = dp;
         D += prow[j] * dp;
     }
+    if (bp->o) {
+        const double *oi = bp->o + (bh * N + i) * d;
+        D = 0.0;
+        for (int64_t c = 0; c < d; ++c) D += doi[c] * oi[c];
+    }
     return D;
 }
 
 /* Full gradients: dq, dk, dv are [B,H,N,d] fp64.  Heads run in parallel;
  * within a head the rows run in order (dk and dv sum over rows). */
 int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                    const uint16_t *dO, int dtype, int64_t B, int64_t H,
-                    int64_t N, int64_t d, int causal, double scale, double *dq,
-                    double *dk, double *dv)
+                    const uint16_t *dO, const uint16_t *o, int dtype, int64_t B,
+                    int64_t H, int64_t N, int64_t d, int causal, double scale,
+                    double *dq, double *dk, double *dv)
 {
     bproblem bp;
-    int rc = load_bproblem(&bp, q, k, v, dO, dtype, B, H, N, d, causal, scale);
+    int rc = load_bproblem(&bp, q, k, v, dO, o, dtype, B, H, N, d, causal, scale);
     if (rc) return rc;
     const int64_t n = B * H * N * d;
     for (int64_t t = 0; t < n; ++t) dq[t] = dk[t] = dv[t] = 0.0;
@@ -535,8 +554,8 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  * needs P_ij and D_i of every query row of its head, so those heads' rows
  * are evaluated once first (lse_i and D_i kept per row). */
 int oracle_attn_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                         const uint16_t *dO, int dtype, int64_t B, int64_t H,
-                         int64_t N, int64_t d, int causal, double scale,
+                         const uint16_t *dO, const uint16_t *o, int dtype, int64_t B,
+                         int64_t H, int64_t N, int64_t d, int causal, double scale,
                          const int64_t *qrows, int64_t n_q, const int64_t *krows,
                          int64_t n_k, double *dq_rows, double *dk_rows,
                          double *dv_rows)
@@ -547,7 +566,7 @@ int oracle_attn_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v
     for (int64_t t = 0; t < n_k; ++t)
         if (krows[t] < 0 || krows[t] >= total) return -1;
     bproblem bp;
-    int rc = load_bproblem(&bp, q, k, v, dO, dtype, B, H, N, d, causal, scale);
+    int rc = load_bproblem(&bp, q, k, v, dO, o, dtype, B, H, N, d, causal, scale);
     if (rc) return rc;
     int fail = 0;
     /* per-row D_i of every head that a sampled key belongs to */

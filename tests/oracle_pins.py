@@ -265,6 +265,33 @@ def pin_bwd_rows(orc) -> bool:
     return ok
 
 
+def pin_bwd_given_o(orc) -> bool:
+    """With a given 16-bit o the row term becomes dO_i . o_i, so the result
+    moves from the plain gradients by exactly dD_i = dO_i . (o_i - O_i):
+    dq by -scale dD_i (P K)_i, dk by -scale (P^T (dD q))_j, dv not at all."""
+    ok = True
+    for causal in (False, True):
+        q, k, v = _qkv(1, 2, 19, 8, "bf16", seed=18)
+        do = _qkv(1, 2, 19, 8, "bf16", seed=19)[0]
+        ro, _, rp = torch_reference(q, k, v, causal, 0.45)
+        o16 = to_tensor(ro, "bf16")
+        dD = (do.double().numpy() * (o16.double().numpy() - ro)).sum(-1)
+        g0 = orc.attn_bwd(bits(q), bits(k), bits(v), bits(do), "bf16", causal, 0.45)
+        g1 = orc.attn_bwd(bits(q), bits(k), bits(v), bits(do), "bf16", causal, 0.45, o=bits(o16))
+        q64, k64 = q.double().numpy(), k.double().numpy()
+        want_dq = g0[0] - 0.45 * dD[..., None] * (rp @ k64)
+        want_dk = g0[1] - 0.45 * (np.swapaxes(rp, -1, -2) @ (dD[..., None] * q64))
+        ok &= _close(g1[0], want_dq, 1e-12) and _close(g1[1], want_dk, 1e-12)
+        ok &= _close(g1[2], g0[2], 0.0)
+        ok &= float(np.abs(dD).max()) > 1e-6          # the case really moves D
+        r = np.array([0, 7, 18, 20, 37], dtype=np.int64)
+        a, b, c = orc.attn_bwd_rows(bits(q), bits(k), bits(v), bits(do), "bf16", causal, 0.45,
+                                    r, r, o=bits(o16))
+        ok &= _close(a, g1[0].reshape(-1, 8)[r], 1e-12) and _close(b, g1[1].reshape(-1, 8)[r], 1e-12)
+        ok &= _close(c, g1[2].reshape(-1, 8)[r], 1e-12)
+    return ok
+
+
 PINS = {
     "brute_force": pin_brute_force,
     "python_loops": pin_python_loops,
@@ -279,6 +306,7 @@ PINS = {
     "bwd_finite_difference": pin_bwd_finite_difference,
     "bwd_invariants": pin_bwd_invariants,
     "bwd_rows": pin_bwd_rows,
+    "bwd_given_o": pin_bwd_given_o,
 }
 
 

@@ -1,5 +1,5 @@
 """CPU tests of the C-ABI library: it loads, exports every function that
-include/fa_fwd.h declares, and rejects bad arguments on the host, before any
+include/*.h declares, and rejects bad arguments on the host, before any
 HIP call (so these run without a GPU).  No compute call is made here."""
 from __future__ import annotations
 
@@ -12,13 +12,15 @@ import pytest
 import io_aware_transformer_amd as fa
 from tests.conftest import ROOT
 
-HEADER = ROOT / "include" / "fa_fwd.h"
+HEADERS = sorted((ROOT / "include").glob("*.h"))
 
 
 def declared_functions():
-    text = HEADER.read_text()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", h.read_text(), flags=re.S)
+        names |= set(re.findall(r"\b(fa_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
@@ -114,3 +116,54 @@ def test_grid_too_large():
     # B*H*ceil(N/128) above INT_MAX is refused on the host
     assert call(B=1 << 16, H=1 << 16, N=1 << 10, q=1 << 44, k=2 << 44, v=3 << 44,
                 o=4 << 44, lse=5 << 44) == fa.FA_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- backward
+
+DO, WS, DQ, DK, DV = (0x10000 * (i + 6) for i in range(5))
+
+
+def bcall(q=Q, k=K, v=V, o=O, do=DO, lse=L, ws=WS, dq=DQ, dk=DK, dv=DV, B=1, H=1, N=64,
+          d=128, causal=0, scale=0.125, dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_bwd(q, k, v, o, do, lse, ws, dq, dk, dv, B, H, N, d, causal, scale, dtype,
+                     None)
+
+
+def test_workspace_size():
+    # per head: ceil(N/32) blocks of 32 (lse*log2e) + 32 (D) fp32 values
+    assert fa.fa_bwd_workspace_size(1, 1, 1) == 256
+    assert fa.fa_bwd_workspace_size(2, 3, 33) == 2 * 3 * 2 * 256
+    assert fa.fa_bwd_workspace_size(1, 1, 64) == 2 * 256
+    assert fa.fa_bwd_workspace_size(0, 1, 64) == 0
+    assert fa.fa_bwd_workspace_size(1, 1, -3) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(q=0), dict(k=0), dict(v=0), dict(o=0), dict(do=0),
+                                dict(lse=0), dict(ws=0), dict(dq=0), dict(dk=0), dict(dv=0)])
+def test_bwd_null_pointers(kw):
+    assert bcall(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(N=-1), dict(causal=2), dict(scale=math.nan),
+                                dict(dtype=5)])
+def test_bwd_invalid(kw):
+    assert bcall(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(d=32), dict(N=(1 << 22) + 1, q=1 << 40,
+                                k=2 << 40, v=3 << 40, o=4 << 40, do=5 << 40, lse=6 << 40,
+                                ws=7 << 40, dq=8 << 40, dk=9 << 40, dv=10 << 40)])
+def test_bwd_unsupported(kw):
+    assert bcall(**kw) == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(q=Q + 2), dict(do=DO + 8), dict(ws=WS + 4),
+                                dict(dq=DQ + 2), dict(dv=DV + 6), dict(lse=L + 1)])
+def test_bwd_misaligned(kw):
+    assert bcall(**kw) == fa.FA_ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("kw", [dict(dq=Q), dict(dk=K + 32), dict(dv=DO), dict(ws=L),
+                                dict(dq=DK), dict(ws=DV + 16), dict(dk=O + 256)])
+def test_bwd_overlaps(kw):
+    assert bcall(**kw) == fa.FA_ERR_INVALID_ARG

@@ -338,13 +338,15 @@ MUTANTS = [
      "const double pij = exp(scale * dot);", "bwd rows: P without lse"),
     ("out[c] += scale * ds * kh[j * d + c];", "out[c] += ds * kh[j * d + c];",
      "bwd rows: dQ without scale"),
+    ("for (int64_t c = 0; c < d; ++c) D += doi[c] * oi[c];",
+     "for (int64_t c = 0; c < d; ++c) D += doi[c] * oi[0];", "bwd: given-o row term index"),
 ]
 
 
 # ---------------------------------------------------------------- gradients
 
 @pytest.mark.parametrize("name", ["bwd_autograd", "bwd_finite_difference", "bwd_invariants",
-                                  "bwd_rows"])
+                                  "bwd_rows", "bwd_given_o"])
 def test_bwd_pin(oracle_mod, name):
     assert PINS[name](oracle_mod)
 
