@@ -8,11 +8,12 @@ to stderr.
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10]
                   [--workload n8k_causal_peaky] [--secondary n4k_causal]
-                  [--no-cpu-baseline] [--mode copy]
+                  [--backward n8k_causal_peaky] [--no-cpu-baseline] [--mode copy]
 
 The headline workload is B=1 H=32 N=8192 d=128 bf16 causal with Q,K x3;
-B=2 H=16 N=4096 d=128 bf16 causal is reported beside it.  FLOP =
-4*B*H*N^2*d, halved when causal.
+B=2 H=16 N=4096 d=128 bf16 causal is reported beside it, and the backward
+pass (fa_bwd) of the headline workload under "backward".  FLOP =
+4*B*H*N^2*d, halved when causal (backward: 2.5 times that).
 """
 from __future__ import annotations
 
@@ -104,6 +105,47 @@ def time_workload(w, steps: int, warmup: int, seed: int = 0):
         "inputs": (q, k, v),
         "outputs": (o, lse),
     }
+
+
+def time_backward(w, steps: int, warmup: int, seed: int = 0):
+    """fa_bwd on the workload: (o, lse) from one fa_fwd, a seeded dO, then
+    `steps` timed backward calls (HIP events on the launch stream)."""
+    import torch
+    import io_aware_transformer_amd as fa
+    from io_aware_transformer_amd.inputs import make_qkv, make_workload
+
+    dev = torch.device("cuda", 0)
+    q, k, v = (t.to(dev) for t in make_workload(w, seed=seed))
+    do = make_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=seed + 12345)[0].to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    dt = fa.FA_DTYPE_F16 if w.dtype == "f16" else fa.FA_DTYPE_BF16
+    st = fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, int(w.causal), w.scale, dt, stream)
+    if st != fa.FA_OK:
+        raise fa.FaError(st)
+    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N) // 4, dtype=torch.float32,
+                     device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+
+    def launch():
+        st = fa.fa_bwd(q, k, v, o, do, lse, ws, dq, dk, dv, w.B, w.H, w.N, w.d, int(w.causal),
+                       w.scale, dt, stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        launch()
+        b.record(stream)
+    torch.cuda.synchronize(dev)
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"ms_mean": sum(per) / len(per), "ms_median": per[len(per) // 2], "ms_min": per[0]}
 
 
 def cpu_baseline(w, inputs, outputs, target_s: float):
@@ -212,6 +254,8 @@ def main() -> int:
     ap.add_argument("--workload", default="n8k_causal_peaky")
     ap.add_argument("--secondary", default="n4k_causal",
                     help="second workload reported beside the headline ('none' to skip)")
+    ap.add_argument("--backward", default="n8k_causal_peaky",
+                    help="workload whose backward pass is reported beside ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench")
@@ -285,6 +329,23 @@ def main() -> int:
                              "kernel_us_mean": round(r2["kernel_ms_mean"] * 1e3, 2),
                              "frac": round(a2 / PEAK_BF16_TFLOPS, 4)}
         del r2
+
+    if args.backward and args.backward != "none":
+        wb = WORKLOADS[args.backward]
+        rb = time_backward(wb, args.steps, args.warmup)
+        # algorithmic backward FLOP: five N x N x d products (S recomputed,
+        # dV, dP, dQ, dK) = 2.5 x the forward's four-d-per-score count
+        fb = 2.5 * wb.flops
+        tb = fb / (rb["ms_mean"] * 1e-3) / 1e12
+        log(f"bench: backward {wb.name} mean {rb['ms_mean']*1e3:.1f} us, {tb:.1f} TFLOP/s "
+            f"({100*tb/PEAK_BF16_TFLOPS:.1f}% of peak)")
+        line["backward"] = {"workload": wb.name, "B": wb.B, "H": wb.H, "N": wb.N, "d": wb.d,
+                            "causal": wb.causal, "flop_per_step": fb,
+                            "ms_mean": round(rb["ms_mean"], 5),
+                            "ms_median": round(rb["ms_median"], 5),
+                            "tflops": round(tb, 2), "frac": round(tb / PEAK_BF16_TFLOPS, 4),
+                            "kernels": "fa_bwd_delta_kernel, fa_bwd_dkdv_kernel, "
+                                       "fa_bwd_dq_kernel (7 products executed)"}
 
     if not args.no_cpu_baseline:
         cb, par = cpu_baseline(w, res["inputs"], res["outputs"], args.cpu_seconds)
