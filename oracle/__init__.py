@@ -35,6 +35,10 @@ Functions and what pins them (tests/test_oracle.py):
                   -scale P^T (dD q), dv unchanged)
   attn_bwd_rows   the same on sampled query rows (dQ) and key rows (dK, dV)
                   -- agreement with attn_bwd
+  attn_fwd_masked sliding window (wl, wr) and per-batch valid lengths
+                  ([P-baidu] §8 mask kinds) -- the unmasked and causal cases
+                  of attn_fwd, padded batches against their unpadded slices,
+                  library softmax with an explicit mask matrix
   decode          binary16 / bfloat16 decoders -- all 65536 patterns vs a
                   library cast, hand-checked values
 """
@@ -89,9 +93,11 @@ def _bind(lib):
     lib.oracle_attn_bwd.argtypes = [p, p, p, p, p, i32, i64, i64, i64, i64, i32, f64, p, p, p]
     lib.oracle_attn_bwd_rows.argtypes = [p, p, p, p, p, i32, i64, i64, i64, i64, i32, f64,
                                          p, i64, p, i64, p, p, p]
+    lib.oracle_attn_fwd_masked.argtypes = [p, p, p, i32, i64, i64, i64, i64, i64, i64, p,
+                                           f64, p, p]
     for name in ("oracle_decode", "oracle_num_threads", "oracle_attn_fwd",
                  "oracle_attn_fwd_rows", "oracle_attn_probs", "oracle_attn_fwd_tiled",
-                 "oracle_attn_bwd", "oracle_attn_bwd_rows"):
+                 "oracle_attn_bwd", "oracle_attn_bwd_rows", "oracle_attn_fwd_masked"):
         getattr(lib, name).restype = ctypes.c_int
     lib.oracle_softmax_1d.restype = None
     lib.oracle_softmax_online_1d.restype = None
@@ -266,8 +272,30 @@ def _impl_attn_bwd_rows(lib, q, k, v, do, dtype, causal: bool, scale: float,
     return dq, dk, dv
 
 
+def _impl_attn_fwd_masked(lib, q, k, v, dtype, window_left: int, window_right: int,
+                          seqlens, scale: float):
+    """Attention with a sliding window and optional per-batch valid lengths
+    (seqlens: B ints or None).  Rows without keys: o = 0, lse = -inf.
+    Returns (o [B,H,N,d], lse [B,H,N])."""
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    B, H, N, d = _shape(q, k, v)
+    sl = None
+    if seqlens is not None:
+        sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+        if sl.shape != (B,):
+            raise ValueError("seqlens must hold one length per batch element")
+    o = np.empty((B, H, N, d), dtype=np.float64)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    _check(lib.oracle_attn_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _dtype_code(dtype), B, H, N,
+                                      d, int(window_left), int(window_right),
+                                      None if sl is None else _ptr(sl), float(scale),
+                                      _ptr(o), _ptr(lse)), "oracle_attn_fwd_masked")
+    return o, lse
+
+
 _API = ("num_threads", "decode", "softmax_1d", "softmax_online_1d", "attn_fwd",
-        "attn_fwd_rows", "attn_probs", "attn_fwd_tiled", "attn_bwd", "attn_bwd_rows")
+        "attn_fwd_rows", "attn_probs", "attn_fwd_tiled", "attn_bwd", "attn_bwd_rows",
+        "attn_fwd_masked")
 
 
 class Oracle:
@@ -306,3 +334,4 @@ attn_probs = _module_fn("attn_probs")
 attn_fwd_tiled = _module_fn("attn_fwd_tiled")
 attn_bwd = _module_fn("attn_bwd")
 attn_bwd_rows = _module_fn("attn_bwd_rows")
+attn_fwd_masked = _module_fn("attn_fwd_masked")

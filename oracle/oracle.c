@@ -635,3 +635,74 @@ int oracle_attn_bwd_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v
     free_bproblem(&bp);
     return fail ? -2 : 0;
 }
+
+/* ---- mask variants --------------------------------------------------------
+ *
+ * [P-baidu] §8 lists the mask kinds an implementation may have to support:
+ * causal, padding and sliding window.  Readings (the page defines none of
+ * them): query i of batch element b may attend key j when
+ *     max(0, i - wl) <= j <= min(L_b - 1, i + wr),
+ * where wl / wr < 0 drop that side of the window, and L_b (0..N) is the
+ * element's valid length (padding: keys >= L_b are masked, and rows i >= L_b
+ * have no keys at all; their output row is 0 and their lse is -inf).  Causal
+ * is wl < 0, wr = 0.  seqlens (host int32 [B]) may be NULL: every L_b = N.
+ */
+int oracle_attn_fwd_masked(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           int dtype, int64_t B, int64_t H, int64_t N, int64_t d,
+                           int64_t wl, int64_t wr, const int32_t *seqlens,
+                           double scale, double *o, double *lse)
+{
+    if (seqlens)
+        for (int64_t b = 0; b < B; ++b)
+            if (seqlens[b] < 0 || seqlens[b] > N) return -1;
+    problem p;
+    int rc = load_problem(&p, q, k, v, dtype, B, H, N, d, 0, scale);
+    if (rc) return rc;
+    const int64_t rows = B * H * N;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < rows; ++r) {
+                const int64_t bh = r / N, i = r % N, b = bh / H;
+                const int64_t L = seqlens ? seqlens[b] : N;
+                int64_t lo = wl < 0 ? 0 : i - wl;
+                int64_t hi = wr < 0 ? L - 1 : i + wr;
+                if (lo < 0) lo = 0;
+                if (hi > L - 1) hi = L - 1;
+                double *orow = o + r * d;
+                if (i >= L || lo > hi) {
+                    for (int64_t c = 0; c < d; ++c) orow[c] = 0.0;
+                    lse[r] = -INFINITY;
+                    continue;
+                }
+                const double *qi = p.q + r * d;
+                const double *kh = p.k + bh * N * d, *vh = p.v + bh * N * d;
+                double m = -INFINITY;
+                for (int64_t j = lo; j <= hi; ++j) {
+                    double dot = 0.0;
+                    for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
+                    s[j] = scale * dot;
+                    if (s[j] > m) m = s[j];
+                }
+                double l = 0.0;
+                for (int64_t c = 0; c < d; ++c) orow[c] = 0.0;
+                for (int64_t j = lo; j <= hi; ++j) {
+                    const double w = exp(s[j] - m);
+                    l += w;
+                    for (int64_t c = 0; c < d; ++c) orow[c] += w * vh[j * d + c];
+                }
+                for (int64_t c = 0; c < d; ++c) orow[c] /= l;
+                lse[r] = m + log(l);
+            }
+        }
+        free(s);
+    }
+    free_problem(&p);
+    return fail ? -2 : 0;
+}

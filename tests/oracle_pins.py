@@ -292,6 +292,59 @@ def pin_bwd_given_o(orc) -> bool:
     return ok
 
 
+# ---------------------------------------------------------------- masks
+
+def masked_reference(q, k, v, wl, wr, seqlens, scale):
+    """torch fp64 softmax with an explicit boolean mask matrix; rows without
+    keys give o = 0 and lse = -inf."""
+    B, H, N, d = q.shape
+    i = torch.arange(N)[:, None]
+    j = torch.arange(N)[None, :]
+    o = np.zeros((B, H, N, d))
+    lse = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        L = N if seqlens is None else int(seqlens[b])
+        allow = (j < L) & (i < L)
+        if wl >= 0:
+            allow &= j >= i - wl
+        if wr >= 0:
+            allow &= j <= i + wr
+        s = torch.matmul(q[b].double(), k[b].double().transpose(-1, -2).contiguous()) * scale
+        s = s.masked_fill(~allow, float("-inf"))
+        has = allow.any(-1)
+        p = torch.softmax(s[:, has], dim=-1)
+        o[b][:, has.numpy()] = torch.matmul(p, v[b].double()).numpy()
+        lse[b][:, has.numpy()] = torch.logsumexp(s[:, has], dim=-1).numpy()
+    return o, lse
+
+
+def pin_masked(orc) -> bool:
+    ok = True
+    q, k, v = _qkv(3, 2, 23, 8, "f16", seed=20)
+    # no window, no padding = the plain definition; (-1, 0) = causal
+    for causal, (wl, wr) in ((False, (-1, -1)), (True, (-1, 0))):
+        o, lse = orc.attn_fwd_masked(bits(q), bits(k), bits(v), "f16", wl, wr, None, 0.3)
+        ro, rl = orc.attn_fwd(bits(q), bits(k), bits(v), "f16", causal, 0.3)
+        ok &= _close(o, ro, 0.0) and _close(lse, rl, 0.0)
+    # a padded element equals its unpadded slice, on the valid rows
+    lens = [23, 9, 1]
+    o, lse = orc.attn_fwd_masked(bits(q), bits(k), bits(v), "f16", -1, -1, lens, 0.3)
+    for b, L in enumerate(lens):
+        sl = lambda t: t[b:b + 1, :, :L, :].contiguous()
+        ro, rl = orc.attn_fwd(bits(sl(q)), bits(sl(k)), bits(sl(v)), "f16", False, 0.3)
+        ok &= _close(o[b:b + 1, :, :L], ro, 1e-15) and _close(lse[b:b + 1, :, :L], rl, 1e-15)
+        ok &= bool(np.all(o[b, :, L:] == 0.0) and np.all(np.isneginf(lse[b, :, L:])))
+    # sliding windows against a library softmax with an explicit mask
+    for (wl, wr), lens in (((4, 0), None), ((3, 2), [23, 17, 0]), ((0, 0), None),
+                           ((-1, 5), [5, 23, 12])):
+        o, lse = orc.attn_fwd_masked(bits(q), bits(k), bits(v), "f16", wl, wr, lens, 0.3)
+        ro, rl = masked_reference(q, k, v, wl, wr, lens, 0.3)
+        fin = np.isfinite(rl)
+        ok &= _close(o, ro, 1e-12) and bool(np.array_equal(fin, np.isfinite(lse)))
+        ok &= _close(lse[fin], rl[fin], 1e-12)
+    return ok
+
+
 PINS = {
     "brute_force": pin_brute_force,
     "python_loops": pin_python_loops,
@@ -307,6 +360,7 @@ PINS = {
     "bwd_invariants": pin_bwd_invariants,
     "bwd_rows": pin_bwd_rows,
     "bwd_given_o": pin_bwd_given_o,
+    "masked": pin_masked,
 }
 
 

@@ -286,7 +286,9 @@ def test_tiny_workload_against_library(oracle_mod):
 # above must catch every one.  (old text, new text, what the mistake is)
 MUTANTS = [
     ("s[j] = p->scale * dot;", "s[j] = dot;", "dropped scale"),
-    ("double w = exp(s[j] - m);", "double w = exp(m - s[j]);", "sign of the exponent"),
+    ("        double w = exp(s[j] - m);", "        double w = exp(m - s[j]);", "sign of the exponent"),
+    ("const double w = exp(s[j] - m);", "const double w = exp(m - s[j]);",
+     "mask: sign of the exponent"),
     ("p->causal ? i + 1 : N;     /* |A_i| */", "p->causal ? i : N;", "causal off by one"),
     ("p->causal ? i + 1 : N;     /* |A_i| */", "p->causal ? N : N;", "causal mask dropped"),
     ("for (int64_t c = 0; c < d; ++c) o_out[c] /= l;", "", "normalisation dropped"),
@@ -299,7 +301,8 @@ MUTANTS = [
     ("dot += qi[c] * kh[j * d + c];\n        prow[j]",
      "dot += qi[c] * kh[j * d + (d - 1 - c)];\n        prow[j]",
      "bwd: feature index of K reversed in the row weights"),
-    ("if (s[j] > m) m = s[j];", "m = 0.0;", "no max subtraction"),
+    ("        if (s[j] > m) m = s[j];\n    }\n    /* pass 2", "        m = 0.0;\n    }\n    /* pass 2",
+     "no max subtraction"),
     ("ldexp((double)(1024 + f), e - 25)", "ldexp((double)(1024 + f), e - 24)",
      "binary16 exponent bias"),
     ("mag = ldexp((double)f, -24);", "mag = ldexp((double)f, -25);", "binary16 subnormal"),
@@ -340,6 +343,15 @@ MUTANTS = [
      "bwd rows: dQ without scale"),
     ("for (int64_t c = 0; c < d; ++c) D += doi[c] * oi[c];",
      "for (int64_t c = 0; c < d; ++c) D += doi[c] * oi[0];", "bwd: given-o row term index"),
+    ("int64_t lo = wl < 0 ? 0 : i - wl;", "int64_t lo = wl < 0 ? 0 : i - wl + 1;",
+     "mask: window left edge off by one"),
+    ("const int64_t L = seqlens ? seqlens[b] : N;",
+     "const int64_t L = seqlens ? seqlens[b] + (seqlens[b] < N) : N;",
+     "mask: padding keeps key L"),
+    ("int64_t hi = wr < 0 ? L - 1 : i + wr;", "int64_t hi = wr < 0 ? L - 1 : i + wr + 1;",
+     "mask: window right edge off by one"),
+    ("if (hi > L - 1) hi = L - 1;", "if (hi > N - 1) hi = N - 1;", "mask: window ignores padding"),
+    ("if (i >= L || lo > hi) {", "if (lo > hi) {", "mask: padded rows not emptied"),
 ]
 
 
@@ -382,6 +394,32 @@ def test_bwd_two_key_closed_form(oracle_mod):
         assert dq[0, 0, i, 0] == pytest.approx(want, abs=1e-15)
     assert dv[0, 0, 0, 0] == pytest.approx(dov[0] * w[0] + dov[1] * w[1], abs=1e-15)
     assert dv[0, 0, 1, 0] == pytest.approx(dov[0] * (1 - w[0]) + dov[1] * (1 - w[1]), abs=1e-15)
+
+
+# ---------------------------------------------------------------- masks
+
+def test_masked_pin(oracle_mod):
+    assert PINS["masked"](oracle_mod)
+
+
+@pytest.mark.parametrize("wl,wr", [(-1, -1), (-1, 0), (0, 0), (7, 0), (7, 3), (-1, 4), (40, 40)])
+@pytest.mark.parametrize("with_lens", [False, True])
+def test_masked_windows(oracle_mod, wl, wr, with_lens):
+    from tests.oracle_pins import masked_reference
+    q, k, v = make_qkv(2, 2, 37, 16, "bf16", seed=wl * 7 + wr + 100)
+    lens = [37, 20] if with_lens else None
+    o, lse = oracle_mod.attn_fwd_masked(bits(q), bits(k), bits(v), "bf16", wl, wr, lens, 0.25)
+    ro, rl = masked_reference(q, k, v, wl, wr, lens, 0.25)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(np.isfinite(lse), np.isfinite(rl))
+    fin = np.isfinite(rl)
+    np.testing.assert_allclose(lse[fin], rl[fin], rtol=0, atol=1e-12)
+
+
+def test_masked_rejects_bad_lengths(oracle_mod):
+    q, k, v = make_qkv(2, 1, 8, 4, "f16", seed=1)
+    with pytest.raises(RuntimeError):
+        oracle_mod.attn_fwd_masked(bits(q), bits(k), bits(v), "f16", -1, -1, [8, 9], 0.5)
 
 
 @pytest.fixture(scope="module")
