@@ -8,11 +8,14 @@ to stderr.
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10]
                   [--workload n8k_causal_peaky] [--secondary n4k_causal]
-                  [--backward n8k_causal_peaky] [--no-cpu-baseline] [--mode copy]
+                  [--backward n8k_causal_peaky] [--window n8k_causal_peaky:1023:0]
+                  [--no-cpu-baseline] [--mode copy]
 
 The headline workload is B=1 H=32 N=8192 d=128 bf16 causal with Q,K x3;
 B=2 H=16 N=4096 d=128 bf16 causal is reported beside it, and the backward
-pass (fa_bwd) of the headline workload under "backward".  FLOP =
+pass (fa_bwd) of the headline workload under "backward", and a sliding-window
+forward (fa_fwd_window, each query sees the 1024 keys ending at itself) under
+"window".  FLOP =
 4*B*H*N^2*d, halved when causal (backward: 2.5 times that).
 """
 from __future__ import annotations
@@ -148,6 +151,46 @@ def time_backward(w, steps: int, warmup: int, seed: int = 0):
     return {"ms_mean": sum(per) / len(per), "ms_median": per[len(per) // 2], "ms_min": per[0]}
 
 
+def time_window(w, window_left: int, window_right: int, steps: int, warmup: int,
+                seed: int = 0):
+    """fa_fwd_window on the workload's inputs with a sliding window and no
+    length mask.  FLOP counts only the allowed (query, key) pairs."""
+    import torch
+    import io_aware_transformer_amd as fa
+    from io_aware_transformer_amd.inputs import make_workload
+
+    dev = torch.device("cuda", 0)
+    q, k, v = (t.to(dev) for t in make_workload(w, seed=seed))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    dt = fa.FA_DTYPE_F16 if w.dtype == "f16" else fa.FA_DTYPE_BF16
+
+    def launch():
+        st = fa.fa_fwd_window(q, k, v, o, lse, w.B, w.H, w.N, w.d, window_left, window_right,
+                              None, w.scale, dt, stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        launch()
+        b.record(stream)
+    torch.cuda.synchronize(dev)
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    i = torch.arange(w.N, dtype=torch.float64)
+    lo = torch.clamp(i - window_left, min=0) if window_left >= 0 else torch.zeros_like(i)
+    hi = torch.clamp(i + window_right, max=w.N - 1) if window_right >= 0 else torch.full_like(i, w.N - 1)
+    pairs = float((hi - lo + 1).sum()) * w.B * w.H
+    return {"ms_mean": sum(per) / len(per), "ms_median": per[len(per) // 2],
+            "flop": 4.0 * w.d * pairs}
+
+
 def cpu_baseline(w, inputs, outputs, target_s: float):
     """The fp64 oracle on a bounded, evenly spaced sample of query rows of
     the same workload, timed on the host cores.  The same rows double as a
@@ -256,6 +299,9 @@ def main() -> int:
                     help="second workload reported beside the headline ('none' to skip)")
     ap.add_argument("--backward", default="n8k_causal_peaky",
                     help="workload whose backward pass is reported beside ('none' to skip)")
+    ap.add_argument("--window", default="n8k_causal_peaky:1023:0",
+                    help="WORKLOAD:LEFT:RIGHT sliding-window forward reported beside "
+                         "('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench")
@@ -346,6 +392,17 @@ def main() -> int:
                             "tflops": round(tb, 2), "frac": round(tb / PEAK_BF16_TFLOPS, 4),
                             "kernels": "fa_bwd_delta_kernel, fa_bwd_dkdv_kernel, "
                                        "fa_bwd_dq_kernel (7 products executed)"}
+
+    if args.window and args.window != "none":
+        wname, wl, wr = args.window.split(":")
+        ww = WORKLOADS[wname]
+        rw = time_window(ww, int(wl), int(wr), args.steps, args.warmup)
+        tw = rw["flop"] / (rw["ms_mean"] * 1e-3) / 1e12
+        log(f"bench: window ({wl},{wr}) on {ww.name} mean {rw['ms_mean']*1e3:.1f} us, "
+            f"{tw:.1f} TFLOP/s of allowed pairs")
+        line["window"] = {"workload": ww.name, "window_left": int(wl), "window_right": int(wr),
+                          "flop_per_step": rw["flop"], "ms_mean": round(rw["ms_mean"], 5),
+                          "tflops": round(tw, 2), "frac": round(tw / PEAK_BF16_TFLOPS, 4)}
 
     if not args.no_cpu_baseline:
         cb, par = cpu_baseline(w, res["inputs"], res["outputs"], args.cpu_seconds)

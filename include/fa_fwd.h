@@ -80,6 +80,24 @@ fa_status fa_fwd(const void *q, const void *k, const void *v, void *o,
                  float *lse, int B, int H, int N, int d, int causal,
                  float scale, fa_dtype dtype, hipStream_t stream);
 
+/* Forward pass with a sliding window and per-batch valid lengths, the mask
+ * kinds besides causal that "FlashAttention 优化原理与实现要点解析" §8 lists
+ * (sliding-window and padding masks; the page defines neither, so):
+ *   query i of batch element b attends key j when
+ *       max(0, i - window_left) <= j <= min(L_b - 1, i + window_right)
+ *   window_left, window_right >= 0, or -1 for no limit on that side
+ *     (-1, -1) is fa_fwd non-causal and (-1, 0) is fa_fwd causal;
+ *   seqlens: device int32 [B] of valid lengths L_b (values clamped to
+ *     0..N), or NULL for L_b = N; keys j >= L_b are padding;
+ *   rows i >= L_b attend nothing: o row = 0, lse = -inf.
+ * Other arguments, layouts and errors as fa_fwd; also FA_ERR_INVALID_ARG for
+ * a window side below -1 and FA_ERR_MISALIGNED for seqlens not 4-byte
+ * aligned.  seqlens is only read. */
+fa_status fa_fwd_window(const void *q, const void *k, const void *v, void *o,
+                        float *lse, int B, int H, int N, int d, int window_left,
+                        int window_right, const int *seqlens, float scale,
+                        fa_dtype dtype, hipStream_t stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *fa_status_string(int status);
 

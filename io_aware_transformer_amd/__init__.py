@@ -10,6 +10,8 @@ C entry points mirrored here with the same names and argument order:
   fa_fwd_f16(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> status
   fa_fwd_bf16(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> status
   fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream) -> status
+  fa_fwd_window(q, k, v, o, lse, B, H, N, d, window_left, window_right, seqlens,
+                scale, dtype, stream) -> status
   fa_bwd(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale,
          dtype, stream) -> status
   fa_bwd_workspace_size(B, H, N) -> bytes
@@ -32,8 +34,8 @@ FA_ERR_LAUNCH = -4
 FA_DTYPE_F16 = 0
 FA_DTYPE_BF16 = 1
 
-EXPORTED = ("fa_fwd_f16", "fa_fwd_bf16", "fa_fwd", "fa_status_string", "fa_bwd",
-            "fa_bwd_workspace_size")
+EXPORTED = ("fa_fwd_f16", "fa_fwd_bf16", "fa_fwd", "fa_fwd_window", "fa_status_string",
+            "fa_bwd", "fa_bwd_workspace_size")
 
 _lib = None
 
@@ -67,6 +69,8 @@ def load():
         getattr(lib, n).restype = ctypes.c_int
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_fwd_window.argtypes = [p, p, p, p, p, i, i, i, i, i, i, p, f, i, p]
+    lib.fa_fwd_window.restype = ctypes.c_int
     lib.fa_bwd.argtypes = [p] * 10 + [i, i, i, i, i, f, i, p]
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd_workspace_size.argtypes = [i, i, i]
@@ -105,6 +109,13 @@ def fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream=None) -> in
     return load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
                          int(N), int(d), int(causal), float(scale), int(dtype),
                          _stream(stream))
+
+
+def fa_fwd_window(q, k, v, o, lse, B, H, N, d, window_left, window_right, seqlens, scale,
+                  dtype, stream=None) -> int:
+    return load().fa_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                int(N), int(d), int(window_left), int(window_right),
+                                _ptr(seqlens), float(scale), int(dtype), _stream(stream))
 
 
 def fa_bwd(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale, dtype,

@@ -203,13 +203,21 @@ __device__ __forceinline__ float half_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int DT, int D, bool CAUSAL>
+// MODE 0: every key; 1: causal (key <= query); 2: window and valid lengths,
+// key j allowed for query i of batch element b when
+// max(0, i - wl) <= j <= min(L_b - 1, i + wr) (wl / wr < 0: that side open;
+// L_b = LENS[b] clamped to [0, N], or N without LENS); rows i >= L_b have no
+// keys and get o = 0, lse = -inf.  Modes 0 and 1 ignore H, wl, wr, LENS.
+template <int DT, int D, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                    const u16 *__restrict__ V, u16 *__restrict__ O,
                    float *__restrict__ LSE, int BH, int N, int nqb, float c,
-                   unsigned qand, unsigned qxor)
+                   unsigned qand, unsigned qxor, int H, int wl, int wr,
+                   const int *__restrict__ LENS)
 {
+    constexpr bool CAUSAL = MODE == 1;
+    constexpr bool GEN = MODE == 2;
     using E = Elem<DT>;
     using T = Tile<D>;
     constexpr int KT = D / 16;    // MFMA k-steps over d
@@ -268,10 +276,41 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
     const int n_keys_tiles = (N + kBC - 1) / kBC;      // compute steps over all keys
     const int n_steps = CAUSAL ? min(n_keys_tiles, (qblk + 1) * (kBR / kBC)) : n_keys_tiles;
-    const int n_tiles = (n_steps + kNSub - 1) / kNSub; // LDS tiles of kLT keys
-    // tiles this wave computes: causal rows q0..q0+31 need keys <= q0+31
+    int t_begin = 0;                                   // LDS tiles [t_begin, n_tiles)
+    int n_tiles = (n_steps + kNSub - 1) / kNSub;       // of kLT keys
+    // steps this wave computes: causal rows q0..q0+31 need keys <= q0+31
     const int n_w = (q0 >= N) ? 0 : (CAUSAL ? min(n_steps, (q0 + kRowsPerWave - 1) / kBC + 1)
                                             : n_steps);
+    // MODE 2: valid length of this batch element, the work-group's and this
+    // wave's key ranges (in steps j_lo..j_hi), and the per-lane key bounds
+    int len = N, j_lo = 0, j_hi = -1, klo_row = 0, khi_row = -1;
+    if constexpr (GEN) {
+        len = LENS ? min(max(LENS[bh / H], 0), N) : N;
+        const int r0 = qblk * kBR, r1 = min(r0 + kBR, len) - 1;
+        if (r0 > r1) {                                 // no valid row in the work-group
+            if (qrow < N) {
+                u16 *orow = O + head + (size_t)qrow * D;
+                const u32x2 z = {0u, 0u};
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) *(u32x2 *)(orow + 32 * db + 8 * g + 4 * hh) = z;
+                if (hh == 0) LSE[(size_t)bh * N + qrow] = neg_inf();
+            }
+            return;
+        }
+        const int klo = wl < 0 ? 0 : max(0, r0 - wl);
+        const int khi = wr < 0 ? len - 1 : min(len - 1, r1 + wr);
+        t_begin = (klo / kBC) / kNSub;
+        n_tiles = (khi / kBC) / kNSub + 1;
+        if (q0 < len) {
+            const int w1 = min(q0 + kRowsPerWave, len) - 1;
+            j_lo = (wl < 0 ? 0 : max(0, q0 - wl)) / kBC;
+            j_hi = (wr < 0 ? len - 1 : min(len - 1, w1 + wr)) / kBC;
+        }
+        klo_row = wl < 0 ? 0 : qrow - wl;
+        khi_row = wr < 0 ? len - 1 : min(len - 1, qrow + wr);
+    }
 
     // ---- HBM -> LDS tile loads (each wave moves its share, 1 KB per load)
     // One of this wave's 1 KB loads of a tile: n < kLoadsPerWave is K, the
@@ -368,7 +407,9 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = t * kBC + 32 * kb + acc_row(r, hh);
-                const bool keep = key < N && (!CAUSAL || key <= qrow);
+                bool keep;
+                if constexpr (GEN) keep = key >= klo_row && key <= khi_row;
+                else keep = key < N && (!CAUSAL || key <= qrow);
                 if (!keep) s[kb][r] = neg_inf();
             }
     };
@@ -463,7 +504,16 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     };
 
     auto tile_masked = [&](int t) {
-        const bool mk = (CAUSAL && t * kBC + kBC - 1 > q0) || (t * kBC + kBC > N);
+        bool mk;
+        if constexpr (GEN) {
+            // every row of the wave keeps every key of the step?
+            const int w1 = q0 + kRowsPerWave - 1;
+            const bool lo_ok = wl < 0 || t * kBC >= w1 - wl;
+            const bool hi_ok = t * kBC + kBC - 1 <= (wr < 0 ? len - 1 : min(len - 1, q0 + wr));
+            mk = !(lo_ok && hi_ok);
+        } else {
+            mk = (CAUSAL && t * kBC + kBC - 1 > q0) || (t * kBC + kBC > N);
+        }
         return __builtin_amdgcn_readfirstlane((int)mk) != 0;
     };
 
@@ -475,7 +525,8 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     // share.  After the last tile the loads are aimed out of range (zero
     // fill of a buffer nobody reads, no memory traffic).
 #pragma unroll
-    for (int n = 0; n < 2 * T::kLoadsPerWave; ++n) issue_one(n, Buf<0>{}, Buf<2>{}, 0);
+    for (int n = 0; n < 2 * T::kLoadsPerWave; ++n)
+        issue_one(n, Buf<0>{}, Buf<2>{}, t_begin * kLT * T::kRowBytes);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -486,7 +537,10 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 #pragma unroll
         for (int u = 0; u < kNSub; ++u) {
             const int j = kNSub * t + u;
-            if (j < n_w) {
+            bool run;
+            if constexpr (GEN) run = j >= j_lo && j <= j_hi;
+            else run = j < n_w;
+            if (run) {
                 sub = u;
                 u32x4 pk[PT];
                 __builtin_amdgcn_s_setprio(2);
@@ -511,16 +565,27 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         __syncthreads();
     };
 
-    for (int t = 0; t < n_tiles; t += 2) {
+    for (int t = t_begin; t < n_tiles; t += 2) {
         tile(Buf<0>{}, t);
         if (t + 1 < n_tiles) tile(Buf<1>{}, t + 1);
     }
 
     // ---- epilogue: one division per row, 16-bit O, fp32 lse
-    if (n_w > 0) {
+    if constexpr (GEN) {
+        if (qrow >= len && qrow < N) {                 // rows without keys
+            u16 *orow = O + head + (size_t)qrow * D;
+            const u32x2 z = {0u, 0u};
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) *(u32x2 *)(orow + 32 * db + 8 * g + 4 * hh) = z;
+            if (hh == 0) LSE[(size_t)bh * N + qrow] = neg_inf();
+        }
+    }
+    if (GEN ? (q0 < len) : (n_w > 0)) {
         const float lht = half_sum(lh);
         const float lt = (DT == FA_DTYPE_BF16) ? half_sum(l) : lht;
-        if (qrow < N) {
+        if (GEN ? (qrow < len) : (qrow < N)) {
             const float inv = 1.f / lht;
             u16 *orow = O + head + (size_t)qrow * D;
 #pragma unroll
@@ -539,13 +604,17 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 }
 
 typedef void (*kernel_fn)(const u16 *, const u16 *, const u16 *, u16 *, float *,
-                          int, int, int, float, unsigned, unsigned);
+                          int, int, int, float, unsigned, unsigned, int, int, int,
+                          const int *);
 
 template <int DT>
-kernel_fn pick(int d, int causal)
+kernel_fn pick(int d, int mode)
 {
-    if (d == 64) return causal ? fa_fwd_kernel<DT, 64, true> : fa_fwd_kernel<DT, 64, false>;
-    return causal ? fa_fwd_kernel<DT, 128, true> : fa_fwd_kernel<DT, 128, false>;
+    if (d == 64)
+        return mode == 0 ? fa_fwd_kernel<DT, 64, 0>
+             : mode == 1 ? fa_fwd_kernel<DT, 64, 1> : fa_fwd_kernel<DT, 64, 2>;
+    return mode == 0 ? fa_fwd_kernel<DT, 128, 0>
+         : mode == 1 ? fa_fwd_kernel<DT, 128, 1> : fa_fwd_kernel<DT, 128, 2>;
 }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
@@ -556,20 +625,23 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
 
 }  // namespace
 
-extern "C" fa_status fa_fwd(const void *q, const void *k, const void *v, void *o,
-                            float *lse, int B, int H, int N, int d, int causal,
-                            float scale, fa_dtype dtype, hipStream_t stream)
+namespace {
+
+// Validation shared by every forward entry point, then one launch of the
+// kernel for `mode` (0 full, 1 causal, 2 window / valid lengths).
+fa_status launch_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                     int H, int N, int d, int mode, int wl, int wr, const int *lens,
+                     float scale, fa_dtype dtype, hipStream_t stream)
 {
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
-    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
     if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
     if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (N > FA_MAX_N) return FA_ERR_UNSUPPORTED;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
         return FA_ERR_MISALIGNED;
-    if ((uintptr_t)lse & 3) return FA_ERR_MISALIGNED;
+    if (((uintptr_t)lse | (uintptr_t)lens) & 3) return FA_ERR_MISALIGNED;
 
     const long long BH = (long long)B * H;
     const long long nqb = (N + kBR - 1) / kBR;
@@ -582,9 +654,12 @@ extern "C" fa_status fa_fwd(const void *q, const void *k, const void *v, void *o
         overlaps(lse, lbytes, k, tbytes) || overlaps(lse, lbytes, v, tbytes) ||
         overlaps(lse, lbytes, o, tbytes))
         return FA_ERR_INVALID_ARG;
+    if (lens && (overlaps(o, tbytes, lens, (size_t)B * 4) ||
+                 overlaps(lse, lbytes, lens, (size_t)B * 4)))
+        return FA_ERR_INVALID_ARG;
 
-    kernel_fn fn = (dtype == FA_DTYPE_F16) ? pick<FA_DTYPE_F16>(d, causal)
-                                           : pick<FA_DTYPE_BF16>(d, causal);
+    kernel_fn fn = (dtype == FA_DTYPE_F16) ? pick<FA_DTYPE_F16>(d, mode)
+                                           : pick<FA_DTYPE_BF16>(d, mode);
     // Scores are always taken with a positive multiplier c: scale < 0 negates
     // Q exactly (sign bits) and scale == 0 zeroes Q (every score 0, every
     // allowed key weighted equally); c = |scale| log2(e), or log2(e) for 0.
@@ -592,14 +667,41 @@ extern "C" fa_status fa_fwd(const void *q, const void *k, const void *v, void *o
     float c = mag * 1.44269504088896340736f;
     unsigned qand = (scale == 0.f) ? 0u : 0xffffffffu;
     unsigned qxor = (scale < 0.f) ? 0x80008000u : 0u;
-    int bh_i = (int)BH, n_i = N, nqb_i = (int)nqb;
+    int bh_i = (int)BH, n_i = N, nqb_i = (int)nqb, h_i = H, wl_i = wl, wr_i = wr;
     const void *qp = q, *kp = k, *vp = v;
     void *op = o;
     float *lp = lse;
-    void *args[] = {&qp, &kp, &vp, &op, &lp, &bh_i, &n_i, &nqb_i, &c, &qand, &qxor};
+    const int *lensp = lens;
+    void *args[] = {&qp, &kp, &vp, &op, &lp, &bh_i, &n_i, &nqb_i, &c, &qand, &qxor,
+                    &h_i, &wl_i, &wr_i, &lensp};
     hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)grid), dim3(kThreads),
                                    args, 0, stream);
     return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" fa_status fa_fwd(const void *q, const void *k, const void *v, void *o,
+                            float *lse, int B, int H, int N, int d, int causal,
+                            float scale, fa_dtype dtype, hipStream_t stream)
+{
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    return launch_fwd(q, k, v, o, lse, B, H, N, d, causal, -1, causal ? 0 : -1, nullptr,
+                      scale, dtype, stream);
+}
+
+extern "C" fa_status fa_fwd_window(const void *q, const void *k, const void *v, void *o,
+                                   float *lse, int B, int H, int N, int d, int window_left,
+                                   int window_right, const int *seqlens, float scale,
+                                   fa_dtype dtype, hipStream_t stream)
+{
+    if (window_left < -1 || window_right < -1) return FA_ERR_INVALID_ARG;
+    // the unwindowed and the causal case without lengths run the tuned kernels
+    int mode = 2;
+    if (!seqlens && window_left == -1 && window_right == -1) mode = 0;
+    if (!seqlens && window_left == -1 && window_right == 0) mode = 1;
+    return launch_fwd(q, k, v, o, lse, B, H, N, d, mode, window_left, window_right, seqlens,
+                      scale, dtype, stream);
 }
 
 extern "C" fa_status fa_fwd_f16(const void *q, const void *k, const void *v, void *o,

@@ -167,3 +167,26 @@ def test_bwd_misaligned(kw):
                                 dict(dq=DK), dict(ws=DV + 16), dict(dk=O + 256)])
 def test_bwd_overlaps(kw):
     assert bcall(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- window / lengths
+
+LENS = 0x10000 * 12
+
+
+def wcall(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=64, d=128, wl=16, wr=0, lens=LENS,
+          scale=0.125, dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_fwd_window(q, k, v, o, lse, B, H, N, d, wl, wr, lens, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [dict(wl=-2), dict(wr=-5), dict(q=0), dict(B=0),
+                                dict(scale=math.inf), dict(dtype=3), dict(o=Q + 256),
+                                dict(lse=LENS), dict(o=LENS - 16)])
+def test_window_invalid(kw):
+    assert wcall(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_window_unsupported_and_misaligned():
+    assert wcall(d=80) == fa.FA_ERR_UNSUPPORTED
+    assert wcall(lens=LENS + 2) == fa.FA_ERR_MISALIGNED
+    assert wcall(v=V + 8) == fa.FA_ERR_MISALIGNED
