@@ -9,13 +9,13 @@ to stderr.
   python bench.py [--gpus 1] [--steps 50] [--warmup 10]
                   [--workload n8k_causal_peaky] [--secondary n4k_causal]
                   [--backward n8k_causal_peaky] [--window n8k_causal_peaky:1023:0]
-                  [--no-cpu-baseline] [--mode copy]
+                  [--split n4k_h4_causal:4] [--no-cpu-baseline] [--mode copy]
 
 The headline workload is B=1 H=32 N=8192 d=128 bf16 causal with Q,K x3;
 B=2 H=16 N=4096 d=128 bf16 causal is reported beside it, and the backward
 pass (fa_bwd) of the headline workload under "backward", and a sliding-window
 forward (fa_fwd_window, each query sees the 1024 keys ending at itself) under
-"window".  FLOP =
+"window", and fa_fwd against fa_fwd_split on a few-head shape under "split".  FLOP =
 4*B*H*N^2*d, halved when causal (backward: 2.5 times that).
 """
 from __future__ import annotations
@@ -191,6 +191,49 @@ def time_window(w, window_left: int, window_right: int, steps: int, warmup: int,
             "flop": 4.0 * w.d * pairs}
 
 
+def time_split(w, num_splits: int, steps: int, warmup: int, seed: int = 0):
+    """fa_fwd and fa_fwd_split(num_splits) on the same inputs, per-call HIP
+    event times (mean of `steps` calls each)."""
+    import torch
+    import io_aware_transformer_amd as fa
+    from io_aware_transformer_amd.inputs import make_workload
+
+    dev = torch.device("cuda", 0)
+    q, k, v = (t.to(dev) for t in make_workload(w, seed=seed))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_fwd_split_workspace_size(w.B, w.H, w.N, w.d, num_splits) // 4,
+                     dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    dt = fa.FA_DTYPE_F16 if w.dtype == "f16" else fa.FA_DTYPE_BF16
+
+    def plain():
+        st = fa.fa_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, int(w.causal), w.scale, dt, stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    def split():
+        st = fa.fa_fwd_split(q, k, v, o, lse, w.B, w.H, w.N, w.d, int(w.causal), w.scale,
+                             num_splits, ws, dt, stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    out = {}
+    for name, fn in (("fa_fwd", plain), ("fa_fwd_split", split)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize(dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize(dev)
+        out[name] = sum(a.elapsed_time(b) for a, b in ev) / steps
+    return out
+
+
 def cpu_baseline(w, inputs, outputs, target_s: float):
     """The fp64 oracle on a bounded, evenly spaced sample of query rows of
     the same workload, timed on the host cores.  The same rows double as a
@@ -302,6 +345,8 @@ def main() -> int:
     ap.add_argument("--window", default="n8k_causal_peaky:1023:0",
                     help="WORKLOAD:LEFT:RIGHT sliding-window forward reported beside "
                          "('none' to skip)")
+    ap.add_argument("--split", default="n4k_h4_causal:4",
+                    help="WORKLOAD:SPLITS split-key forward reported beside ('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench")
@@ -403,6 +448,21 @@ def main() -> int:
         line["window"] = {"workload": ww.name, "window_left": int(wl), "window_right": int(wr),
                           "flop_per_step": rw["flop"], "ms_mean": round(rw["ms_mean"], 5),
                           "tflops": round(tw, 2), "frac": round(tw / PEAK_BF16_TFLOPS, 4)}
+
+    if args.split and args.split != "none":
+        sname, ns = args.split.split(":")
+        wsp = WORKLOADS[sname]
+        rs = time_split(wsp, int(ns), args.steps, args.warmup)
+        ts = wsp.flops / (rs["fa_fwd_split"] * 1e-3) / 1e12
+        tp = wsp.flops / (rs["fa_fwd"] * 1e-3) / 1e12
+        log(f"bench: split {sname} x{ns}: fa_fwd {rs['fa_fwd']*1e3:.1f} us ({tp:.1f} TFLOP/s), "
+            f"fa_fwd_split {rs['fa_fwd_split']*1e3:.1f} us ({ts:.1f} TFLOP/s)")
+        line["split"] = {"workload": wsp.name, "B": wsp.B, "H": wsp.H, "N": wsp.N, "d": wsp.d,
+                         "causal": wsp.causal, "num_splits": int(ns),
+                         "ms_fa_fwd": round(rs["fa_fwd"], 5),
+                         "ms_fa_fwd_split": round(rs["fa_fwd_split"], 5),
+                         "tflops_fa_fwd": round(tp, 2), "tflops_fa_fwd_split": round(ts, 2),
+                         "frac_fa_fwd_split": round(ts / PEAK_BF16_TFLOPS, 4)}
 
     if not args.no_cpu_baseline:
         cb, par = cpu_baseline(w, res["inputs"], res["outputs"], args.cpu_seconds)

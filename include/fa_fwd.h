@@ -33,6 +33,7 @@
 #ifndef FA_FWD_H
 #define FA_FWD_H
 
+#include <stddef.h>
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -97,6 +98,31 @@ fa_status fa_fwd_window(const void *q, const void *k, const void *v, void *o,
                         float *lse, int B, int H, int N, int d, int window_left,
                         int window_right, const int *seqlens, float scale,
                         fa_dtype dtype, hipStream_t stream);
+
+/* Most key segments fa_fwd_split accepts. */
+#define FA_MAX_SPLITS 64
+
+/* Bytes of fp32 workspace fa_fwd_split needs (0 if an argument is invalid):
+ * per non-empty key segment, a normalised fp32 O and an lse per row. */
+size_t fa_fwd_split_workspace_size(int B, int H, int N, int d, int num_splits);
+
+/* Forward pass with the keys of every row split into up to num_splits
+ * segments (each a whole number of 128-key tiles) that separate
+ * work-groups process, then merged per row with the same online-softmax
+ * algebra the tiles use ("FlashAttention 优化原理与实现要点解析" §4.2-§4.3;
+ * the split-K/V decoding of "FlashAttention V2 核心原理与架构设计" §5.1):
+ *     lse = ln sum_s exp(lse_s),   o = sum_s exp(lse_s - lse) o_s.
+ * It computes what fa_fwd computes; it pays off when B*H*ceil(N/256)
+ * work-groups leave compute units idle (few heads, short-to-moderate N).
+ *   num_splits  1 .. FA_MAX_SPLITS
+ *   ws          fa_fwd_split_workspace_size bytes, 16-byte aligned, scratch
+ * Other arguments and errors as fa_fwd (FA_ERR_INVALID_ARG also for
+ * num_splits out of range, a null or overlapping ws; FA_ERR_MISALIGNED for
+ * ws).  Two kernels are enqueued on `stream`. */
+fa_status fa_fwd_split(const void *q, const void *k, const void *v, void *o,
+                       float *lse, int B, int H, int N, int d, int causal,
+                       float scale, int num_splits, float *ws, fa_dtype dtype,
+                       hipStream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *fa_status_string(int status);

@@ -12,6 +12,9 @@ C entry points mirrored here with the same names and argument order:
   fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, stream) -> status
   fa_fwd_window(q, k, v, o, lse, B, H, N, d, window_left, window_right, seqlens,
                 scale, dtype, stream) -> status
+  fa_fwd_split(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, ws,
+               dtype, stream) -> status
+  fa_fwd_split_workspace_size(B, H, N, d, num_splits) -> bytes
   fa_bwd(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale,
          dtype, stream) -> status
   fa_bwd_workspace_size(B, H, N) -> bytes
@@ -34,8 +37,10 @@ FA_ERR_LAUNCH = -4
 FA_DTYPE_F16 = 0
 FA_DTYPE_BF16 = 1
 
-EXPORTED = ("fa_fwd_f16", "fa_fwd_bf16", "fa_fwd", "fa_fwd_window", "fa_status_string",
-            "fa_bwd", "fa_bwd_workspace_size")
+EXPORTED = ("fa_fwd_f16", "fa_fwd_bf16", "fa_fwd", "fa_fwd_window", "fa_fwd_split",
+            "fa_fwd_split_workspace_size", "fa_status_string", "fa_bwd",
+            "fa_bwd_workspace_size")
+FA_MAX_SPLITS = 64
 
 _lib = None
 
@@ -71,6 +76,10 @@ def load():
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_fwd_window.argtypes = [p, p, p, p, p, i, i, i, i, i, i, p, f, i, p]
     lib.fa_fwd_window.restype = ctypes.c_int
+    lib.fa_fwd_split.argtypes = [p, p, p, p, p, i, i, i, i, i, f, i, p, i, p]
+    lib.fa_fwd_split.restype = ctypes.c_int
+    lib.fa_fwd_split_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_fwd_split_workspace_size.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [p] * 10 + [i, i, i, i, i, f, i, p]
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd_workspace_size.argtypes = [i, i, i]
@@ -116,6 +125,18 @@ def fa_fwd_window(q, k, v, o, lse, B, H, N, d, window_left, window_right, seqlen
     return load().fa_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
                                 int(N), int(d), int(window_left), int(window_right),
                                 _ptr(seqlens), float(scale), int(dtype), _stream(stream))
+
+
+def fa_fwd_split(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, ws, dtype,
+                 stream=None) -> int:
+    return load().fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                               int(N), int(d), int(causal), float(scale), int(num_splits),
+                               _ptr(ws), int(dtype), _stream(stream))
+
+
+def fa_fwd_split_workspace_size(B, H, N, d, num_splits) -> int:
+    return int(load().fa_fwd_split_workspace_size(int(B), int(H), int(N), int(d),
+                                                  int(num_splits)))
 
 
 def fa_bwd(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale, dtype,

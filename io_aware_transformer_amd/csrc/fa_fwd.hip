@@ -72,6 +72,7 @@ typedef u16 u16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -207,17 +208,23 @@ __device__ __forceinline__ float half_sum(float x) {
 // key j allowed for query i of batch element b when
 // max(0, i - wl) <= j <= min(L_b - 1, i + wr) (wl / wr < 0: that side open;
 // L_b = LENS[b] clamped to [0, N], or N without LENS); rows i >= L_b have no
-// keys and get o = 0, lse = -inf.  Modes 0 and 1 ignore H, wl, wr, LENS.
+// keys and get o = 0, lse = -inf.  3: one key segment [kseg*y, kseg*(y+1))
+// (y = blockIdx.y) of the window rule with L_b = N; writes the segment's
+// normalised O in fp32 to PO and its lse to PL ([y][b*H+h][row]), rows
+// without keys in the segment 0 and -inf, for a merge kernel to combine.
+// Modes 0 and 1 ignore H, wl, wr, LENS, kseg, PO, PL.
 template <int DT, int D, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                    const u16 *__restrict__ V, u16 *__restrict__ O,
                    float *__restrict__ LSE, int BH, int N, int nqb, float c,
                    unsigned qand, unsigned qxor, int H, int wl, int wr,
-                   const int *__restrict__ LENS)
+                   const int *__restrict__ LENS, int kseg, float *__restrict__ PO,
+                   float *__restrict__ PL)
 {
     constexpr bool CAUSAL = MODE == 1;
-    constexpr bool GEN = MODE == 2;
+    constexpr bool GEN = MODE >= 2;
+    constexpr bool SPLIT = MODE == 3;
     using E = Elem<DT>;
     using T = Tile<D>;
     constexpr int KT = D / 16;    // MFMA k-steps over d
@@ -283,33 +290,54 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                                             : n_steps);
     // MODE 2: valid length of this batch element, the work-group's and this
     // wave's key ranges (in steps j_lo..j_hi), and the per-lane key bounds
-    int len = N, j_lo = 0, j_hi = -1, klo_row = 0, khi_row = -1;
+    int len = N, j_lo = 0, j_hi = -1, klo_row = 0, khi_row = -1, kbeg = 0, kend = N;
+    // rows without keys: o = 0 / lse = -inf (or the fp32 partials in mode 3)
+    const size_t prow = ((size_t)blockIdx.y * BH + bh) * N + qrow;
+    auto write_empty = [&]() {
+        if constexpr (SPLIT) {
+            float *po = PO + prow * D;
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) *(f32x4 *)(po + 32 * db + 8 * g + 4 * hh) = z;
+            if (hh == 0) PL[prow] = neg_inf();
+        } else {
+            u16 *orow = O + head + (size_t)qrow * D;
+            const u32x2 z = {0u, 0u};
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) *(u32x2 *)(orow + 32 * db + 8 * g + 4 * hh) = z;
+            if (hh == 0) LSE[(size_t)bh * N + qrow] = neg_inf();
+        }
+    };
     if constexpr (GEN) {
         len = LENS ? min(max(LENS[bh / H], 0), N) : N;
+        if constexpr (SPLIT) {
+            kbeg = blockIdx.y * kseg;
+            kend = min(N, kbeg + kseg);
+        }
         const int r0 = qblk * kBR, r1 = min(r0 + kBR, len) - 1;
-        if (r0 > r1) {                                 // no valid row in the work-group
-            if (qrow < N) {
-                u16 *orow = O + head + (size_t)qrow * D;
-                const u32x2 z = {0u, 0u};
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) *(u32x2 *)(orow + 32 * db + 8 * g + 4 * hh) = z;
-                if (hh == 0) LSE[(size_t)bh * N + qrow] = neg_inf();
-            }
+        const int klo = max(wl < 0 ? 0 : max(0, r0 - wl), kbeg);
+        const int khi = min(wr < 0 ? len - 1 : min(len - 1, r1 + wr), kend - 1);
+        if (r0 > r1 || klo > khi) {                    // no (row, key) pair in the work-group
+            if (qrow < N) write_empty();
             return;
         }
-        const int klo = wl < 0 ? 0 : max(0, r0 - wl);
-        const int khi = wr < 0 ? len - 1 : min(len - 1, r1 + wr);
         t_begin = (klo / kBC) / kNSub;
         n_tiles = (khi / kBC) / kNSub + 1;
         if (q0 < len) {
             const int w1 = min(q0 + kRowsPerWave, len) - 1;
-            j_lo = (wl < 0 ? 0 : max(0, q0 - wl)) / kBC;
-            j_hi = (wr < 0 ? len - 1 : min(len - 1, w1 + wr)) / kBC;
+            const int wlo = max(wl < 0 ? 0 : max(0, q0 - wl), kbeg);
+            const int whi = min(wr < 0 ? len - 1 : min(len - 1, w1 + wr), kend - 1);
+            if (wlo <= whi) {
+                j_lo = wlo / kBC;
+                j_hi = whi / kBC;
+            }
         }
-        klo_row = wl < 0 ? 0 : qrow - wl;
-        khi_row = wr < 0 ? len - 1 : min(len - 1, qrow + wr);
+        klo_row = max(wl < 0 ? 0 : qrow - wl, kbeg);
+        khi_row = min(wr < 0 ? len - 1 : min(len - 1, qrow + wr), kend - 1);
     }
 
     // ---- HBM -> LDS tile loads (each wave moves its share, 1 KB per load)
@@ -508,8 +536,9 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         if constexpr (GEN) {
             // every row of the wave keeps every key of the step?
             const int w1 = q0 + kRowsPerWave - 1;
-            const bool lo_ok = wl < 0 || t * kBC >= w1 - wl;
-            const bool hi_ok = t * kBC + kBC - 1 <= (wr < 0 ? len - 1 : min(len - 1, q0 + wr));
+            const bool lo_ok = t * kBC >= max(wl < 0 ? 0 : w1 - wl, kbeg);
+            const bool hi_ok = t * kBC + kBC - 1 <=
+                               min(wr < 0 ? len - 1 : min(len - 1, q0 + wr), kend - 1);
             mk = !(lo_ok && hi_ok);
         } else {
             mk = (CAUSAL && t * kBC + kBC - 1 > q0) || (t * kBC + kBC > N);
@@ -572,15 +601,34 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
     // ---- epilogue: one division per row, 16-bit O, fp32 lse
     if constexpr (GEN) {
-        if (qrow >= len && qrow < N) {                 // rows without keys
-            u16 *orow = O + head + (size_t)qrow * D;
-            const u32x2 z = {0u, 0u};
+        if (qrow >= len && qrow < N) write_empty();    // rows without keys
+    }
+    if constexpr (SPLIT) {
+        // the segment's normalised O in fp32 and its lse; rows that met no
+        // key of the segment (row sum 0) are empty
+        if (q0 < len) {
+            const float lht = half_sum(lh);
+            const float lt = (DT == FA_DTYPE_BF16) ? half_sum(l) : lht;
+            if (qrow < len) {
+                if (lht > 0.f) {
+                    const float inv = 1.f / lht;
+                    float *po = PO + prow * D;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+                    for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) *(u32x2 *)(orow + 32 * db + 8 * g + 4 * hh) = z;
-            if (hh == 0) LSE[(size_t)bh * N + qrow] = neg_inf();
+                        for (int g = 0; g < 4; ++g) {
+                            f32x4 x;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) x[e] = oacc[db][4 * g + e] * inv;
+                            *(f32x4 *)(po + 32 * db + 8 * g + 4 * hh) = x;
+                        }
+                    if (hh == 0) PL[prow] = (m + log2f(lt)) * 0.69314718055994530942f;
+                } else {
+                    write_empty();
+                }
+            }
         }
+        return;
     }
     if (GEN ? (q0 < len) : (n_w > 0)) {
         const float lht = half_sum(lh);
@@ -605,16 +653,62 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
 typedef void (*kernel_fn)(const u16 *, const u16 *, const u16 *, u16 *, float *,
                           int, int, int, float, unsigned, unsigned, int, int, int,
-                          const int *);
+                          const int *, int, float *, float *);
+
+template <int DT, int D>
+kernel_fn pick_d(int mode)
+{
+    switch (mode) {
+    case 0: return fa_fwd_kernel<DT, D, 0>;
+    case 1: return fa_fwd_kernel<DT, D, 1>;
+    case 2: return fa_fwd_kernel<DT, D, 2>;
+    default: return fa_fwd_kernel<DT, D, 3>;
+    }
+}
 
 template <int DT>
 kernel_fn pick(int d, int mode)
 {
-    if (d == 64)
-        return mode == 0 ? fa_fwd_kernel<DT, 64, 0>
-             : mode == 1 ? fa_fwd_kernel<DT, 64, 1> : fa_fwd_kernel<DT, 64, 2>;
-    return mode == 0 ? fa_fwd_kernel<DT, 128, 0>
-         : mode == 1 ? fa_fwd_kernel<DT, 128, 1> : fa_fwd_kernel<DT, 128, 2>;
+    return d == 64 ? pick_d<DT, 64>(mode) : pick_d<DT, 128>(mode);
+}
+
+// Merge of the key segments of mode 3, per row ([P-baidu] §4.2-§4.3 and the
+// split-K/V combination of "FlashAttention V2 核心原理与架构设计" §5.1):
+// lse = ln sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s, O rounded once.
+// D / 4 lanes per row, 4 elements each.
+template <int DT, int D>
+__global__ __launch_bounds__(256)
+void fa_fwd_merge_kernel(const float *__restrict__ PO, const float *__restrict__ PL,
+                         u16 *__restrict__ O, float *__restrict__ LSE, long long rows,
+                         int nseg)
+{
+    using E = Elem<DT>;
+    constexpr int LPR = D / 4;
+    constexpr int RPB = 256 / LPR;
+    const long long r = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+    const int part = threadIdx.x % LPR;
+    if (r >= rows) return;
+    float mx = neg_inf();
+    for (int s = 0; s < nseg; ++s) mx = fmaxf(mx, PL[(size_t)s * rows + r]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float sum = 0.f;
+    if (mx != neg_inf()) {
+        for (int s = 0; s < nseg; ++s) {
+            const float ls = PL[(size_t)s * rows + r];
+            if (ls == neg_inf()) continue;
+            const float wgt = __expf(ls - mx);
+            sum += wgt;
+            const f32x4 x = *(const f32x4 *)(PO + ((size_t)s * rows + r) * D + 4 * part);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, x[e], acc[e]);
+        }
+    }
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
+    u32x2 pr;
+    pr[0] = E::pack2(acc[0] * inv, acc[1] * inv);
+    pr[1] = E::pack2(acc[2] * inv, acc[3] * inv);
+    *(u32x2 *)(O + r * D + 4 * part) = pr;
+    if (part == 0) LSE[r] = sum > 0.f ? mx + logf(sum) : neg_inf();
 }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
@@ -629,9 +723,9 @@ namespace {
 
 // Validation shared by every forward entry point, then one launch of the
 // kernel for `mode` (0 full, 1 causal, 2 window / valid lengths).
-fa_status launch_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
-                     int H, int N, int d, int mode, int wl, int wr, const int *lens,
-                     float scale, fa_dtype dtype, hipStream_t stream)
+fa_status validate_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                       int B, int H, int N, int d, const int *lens, float scale,
+                       fa_dtype dtype)
 {
     if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
@@ -657,7 +751,19 @@ fa_status launch_fwd(const void *q, const void *k, const void *v, void *o, float
     if (lens && (overlaps(o, tbytes, lens, (size_t)B * 4) ||
                  overlaps(lse, lbytes, lens, (size_t)B * 4)))
         return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
 
+fa_status launch_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
+                     int H, int N, int d, int mode, int wl, int wr, const int *lens,
+                     float scale, fa_dtype dtype, hipStream_t stream, int nseg = 1,
+                     int kseg = 0, float *po = nullptr, float *pl = nullptr)
+{
+    const fa_status vs = validate_fwd(q, k, v, o, lse, B, H, N, d, lens, scale, dtype);
+    if (vs != FA_OK) return vs;
+    const long long BH = (long long)B * H;
+    const long long nqb = (N + kBR - 1) / kBR;
+    const long long grid = BH * nqb;
     kernel_fn fn = (dtype == FA_DTYPE_F16) ? pick<FA_DTYPE_F16>(d, mode)
                                            : pick<FA_DTYPE_BF16>(d, mode);
     // Scores are always taken with a positive multiplier c: scale < 0 negates
@@ -668,15 +774,47 @@ fa_status launch_fwd(const void *q, const void *k, const void *v, void *o, float
     unsigned qand = (scale == 0.f) ? 0u : 0xffffffffu;
     unsigned qxor = (scale < 0.f) ? 0x80008000u : 0u;
     int bh_i = (int)BH, n_i = N, nqb_i = (int)nqb, h_i = H, wl_i = wl, wr_i = wr;
+    int kseg_i = kseg;
     const void *qp = q, *kp = k, *vp = v;
     void *op = o;
-    float *lp = lse;
+    float *lp = lse, *pop = po, *plp = pl;
     const int *lensp = lens;
     void *args[] = {&qp, &kp, &vp, &op, &lp, &bh_i, &n_i, &nqb_i, &c, &qand, &qxor,
-                    &h_i, &wl_i, &wr_i, &lensp};
-    hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)grid), dim3(kThreads),
-                                   args, 0, stream);
-    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+                    &h_i, &wl_i, &wr_i, &lensp, &kseg_i, &pop, &plp};
+    hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)grid, (unsigned)nseg),
+                                   dim3(kThreads), args, 0, stream);
+    if (e != hipSuccess) return FA_ERR_LAUNCH;
+    if (mode == 3) {
+        const long long rows = BH * N;
+        const int rpb = 256 / (d / 4);
+        const long long g2 = (rows + rpb - 1) / rpb;
+        if (g2 > INT_MAX) return FA_ERR_INVALID_ARG;
+        if (dtype == FA_DTYPE_F16) {
+            if (d == 64)
+                hipLaunchKernelGGL((fa_fwd_merge_kernel<FA_DTYPE_F16, 64>), dim3((unsigned)g2),
+                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nseg);
+            else
+                hipLaunchKernelGGL((fa_fwd_merge_kernel<FA_DTYPE_F16, 128>), dim3((unsigned)g2),
+                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nseg);
+        } else {
+            if (d == 64)
+                hipLaunchKernelGGL((fa_fwd_merge_kernel<FA_DTYPE_BF16, 64>), dim3((unsigned)g2),
+                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nseg);
+            else
+                hipLaunchKernelGGL((fa_fwd_merge_kernel<FA_DTYPE_BF16, 128>), dim3((unsigned)g2),
+                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nseg);
+        }
+        if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+    }
+    return FA_OK;
+}
+
+// Key segment length for num_splits requested splits: a whole number of
+// LDS tiles; the number of non-empty segments can be smaller than asked.
+int split_kseg(int N, int num_splits)
+{
+    const int per = (N + num_splits - 1) / num_splits;
+    return ((per + kLT - 1) / kLT) * kLT;
 }
 
 }  // namespace
@@ -702,6 +840,39 @@ extern "C" fa_status fa_fwd_window(const void *q, const void *k, const void *v, 
     if (!seqlens && window_left == -1 && window_right == 0) mode = 1;
     return launch_fwd(q, k, v, o, lse, B, H, N, d, mode, window_left, window_right, seqlens,
                       scale, dtype, stream);
+}
+
+extern "C" size_t fa_fwd_split_workspace_size(int B, int H, int N, int d, int num_splits)
+{
+    if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128) || num_splits < 1 ||
+        num_splits > FA_MAX_SPLITS)
+        return 0;
+    const int kseg = split_kseg(N, num_splits);
+    const size_t nseg = (size_t)((N + kseg - 1) / kseg);
+    return nseg * (size_t)B * (size_t)H * (size_t)N * (size_t)(d + 1) * sizeof(float);
+}
+
+extern "C" fa_status fa_fwd_split(const void *q, const void *k, const void *v, void *o,
+                                  float *lse, int B, int H, int N, int d, int causal,
+                                  float scale, int num_splits, float *ws, fa_dtype dtype,
+                                  hipStream_t stream)
+{
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (num_splits < 1 || num_splits > FA_MAX_SPLITS || !ws) return FA_ERR_INVALID_ARG;
+    const fa_status vs = validate_fwd(q, k, v, o, lse, B, H, N, d, nullptr, scale, dtype);
+    if (vs != FA_OK) return vs;
+    if ((uintptr_t)ws & 15) return FA_ERR_MISALIGNED;
+    const size_t wsb = fa_fwd_split_workspace_size(B, H, N, d, num_splits);
+    const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * 4;
+    if (overlaps(ws, wsb, q, tb) || overlaps(ws, wsb, k, tb) || overlaps(ws, wsb, v, tb) ||
+        overlaps(ws, wsb, o, tb) || overlaps(ws, wsb, lse, lb))
+        return FA_ERR_INVALID_ARG;
+    const int kseg = split_kseg(N, num_splits);
+    const int nseg = (N + kseg - 1) / kseg;
+    float *po = ws;
+    float *pl = ws + (size_t)nseg * B * H * N * d;
+    return launch_fwd(q, k, v, o, lse, B, H, N, d, 3, -1, causal ? 0 : -1, nullptr, scale,
+                      dtype, stream, nseg, kseg, po, pl);
 }
 
 extern "C" fa_status fa_fwd_f16(const void *q, const void *k, const void *v, void *o,

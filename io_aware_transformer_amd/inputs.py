@@ -70,6 +70,8 @@ WORKLOADS = {
                          note="extra: B2 H16 N4096 d128 bf16, non-causal"),
     "n8k_full": Workload("n8k_full", 1, 32, 8192, 128, "bf16", False,
                          note="extra: B1 H32 N8192 d128 bf16, non-causal"),
+    "n4k_h4_causal": Workload("n4k_h4_causal", 1, 4, 4096, 128, "bf16", True,
+                              note="extra: B1 H4 N4096 d128 bf16, causal (64 Q blocks)"),
 }
 
 

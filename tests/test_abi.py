@@ -190,3 +190,35 @@ def test_window_unsupported_and_misaligned():
     assert wcall(d=80) == fa.FA_ERR_UNSUPPORTED
     assert wcall(lens=LENS + 2) == fa.FA_ERR_MISALIGNED
     assert wcall(v=V + 8) == fa.FA_ERR_MISALIGNED
+
+
+# ---------------------------------------------------------------- split keys
+
+SWS = 0x10000 * 13
+
+
+def scall(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=64, d=128, causal=0, scale=0.125, ns=2,
+          ws=SWS, dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_fwd_split(q, k, v, o, lse, B, H, N, d, causal, scale, ns, ws, dtype, None)
+
+
+def test_split_workspace_size():
+    # segments are whole 128-key tiles: N = 300 in 2 splits -> 256 + 44 keys
+    assert fa.fa_fwd_split_workspace_size(1, 2, 300, 64, 2) == 2 * 2 * 300 * 65 * 4
+    # more splits than tiles: only non-empty segments are counted
+    assert fa.fa_fwd_split_workspace_size(1, 1, 100, 128, 64) == 1 * 100 * 129 * 4
+    assert fa.fa_fwd_split_workspace_size(1, 1, 100, 128, 0) == 0
+    assert fa.fa_fwd_split_workspace_size(1, 1, 100, 128, fa.FA_MAX_SPLITS + 1) == 0
+    assert fa.fa_fwd_split_workspace_size(1, 1, 100, 96, 2) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(ns=0), dict(ns=65), dict(ws=0), dict(causal=3),
+                                dict(q=0), dict(N=0), dict(ws=Q), dict(ws=L - 16)])
+def test_split_invalid(kw):
+    assert scall(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_split_unsupported_and_misaligned():
+    assert scall(d=32) == fa.FA_ERR_UNSUPPORTED
+    assert scall(ws=SWS + 4) == fa.FA_ERR_MISALIGNED
+    assert scall(k=K + 2) == fa.FA_ERR_MISALIGNED
