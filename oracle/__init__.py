@@ -35,6 +35,14 @@ Functions and what pins them (tests/test_oracle.py):
                   -scale P^T (dD q), dv unchanged)
   attn_bwd_rows   the same on sampled query rows (dQ) and key rows (dK, dV)
                   -- agreement with attn_bwd
+  philox4x32_10   the counter-based generator (SC 2011 definition) -- the
+                  published known-answer vectors (tests/golden)
+  dropout_factors keep factors Z_ij (256/T or 0) of the documented mapping
+                  -- the mapping re-derived from philox4x32_10, keep rate
+  attn_fwd_dropout / attn_bwd_dropout  attention with dropout after the
+                  softmax -- p = 0 reproduces attn_fwd / attn_bwd(o), torch
+                  fp64 with an explicit keep matrix, autograd up to the exact
+                  shift of the given-o row term
   attn_fwd_masked sliding window (wl, wr) and per-batch valid lengths
                   ([P-baidu] §8 mask kinds) -- the unmasked and causal cases
                   of attn_fwd, padded batches against their unpadded slices,
@@ -95,9 +103,19 @@ def _bind(lib):
                                          p, i64, p, i64, p, p, p]
     lib.oracle_attn_fwd_masked.argtypes = [p, p, p, i32, i64, i64, i64, i64, i64, i64, p,
                                            f64, p, p]
+    u64 = ctypes.c_uint64
+    u32 = ctypes.c_uint32
+    lib.oracle_philox4x32_10.argtypes = [p, p, p]
+    lib.oracle_philox4x32_10.restype = None
+    lib.oracle_dropout_factors.argtypes = [i64, i64, u64, u32, i32, p]
+    lib.oracle_attn_fwd_dropout.argtypes = [p, p, p, i32, i64, i64, i64, i64, i32, f64, i32,
+                                            u64, u32, p, p]
+    lib.oracle_attn_bwd_dropout.argtypes = [p, p, p, p, p, i32, i64, i64, i64, i64, i32, f64,
+                                            i32, u64, u32, p, p, p]
     for name in ("oracle_decode", "oracle_num_threads", "oracle_attn_fwd",
                  "oracle_attn_fwd_rows", "oracle_attn_probs", "oracle_attn_fwd_tiled",
-                 "oracle_attn_bwd", "oracle_attn_bwd_rows", "oracle_attn_fwd_masked"):
+                 "oracle_attn_bwd", "oracle_attn_bwd_rows", "oracle_attn_fwd_masked",
+                 "oracle_dropout_factors", "oracle_attn_fwd_dropout", "oracle_attn_bwd_dropout"):
         getattr(lib, name).restype = ctypes.c_int
     lib.oracle_softmax_1d.restype = None
     lib.oracle_softmax_online_1d.restype = None
@@ -293,9 +311,63 @@ def _impl_attn_fwd_masked(lib, q, k, v, dtype, window_left: int, window_right: i
     return o, lse
 
 
+def dropout_threshold(p_drop: float) -> int:
+    """T = round((1 - p) * 256): a weight is kept when its byte is below T."""
+    if not (0.0 <= p_drop < 1.0):
+        raise ValueError("dropout probability must lie in [0, 1)")
+    return int(np.floor((1.0 - p_drop) * 256.0 + 0.5))
+
+
+def _impl_philox4x32_10(lib, counter, key):
+    c = np.ascontiguousarray(counter, dtype=np.uint32)
+    kk = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.empty(4, dtype=np.uint32)
+    lib.oracle_philox4x32_10(_ptr(c), _ptr(kk), _ptr(out))
+    return out
+
+
+def _impl_dropout_factors(lib, BH: int, N: int, seed: int, offset: int, T: int):
+    """Z [BH, N, N]: 256/T where element (bh, i, j) is kept, else 0."""
+    z = np.empty((BH, N, N), dtype=np.float64)
+    _check(lib.oracle_dropout_factors(BH, N, int(seed), int(offset), int(T), _ptr(z)),
+           "oracle_dropout_factors")
+    return z
+
+
+def _impl_attn_fwd_dropout(lib, q, k, v, dtype, causal: bool, scale: float, T: int, seed: int,
+                           offset: int):
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    B, H, N, d = _shape(q, k, v)
+    o = np.empty((B, H, N, d), dtype=np.float64)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    _check(lib.oracle_attn_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _dtype_code(dtype), B, H, N,
+                                       d, int(bool(causal)), float(scale), int(T), int(seed),
+                                       int(offset), _ptr(o), _ptr(lse)),
+           "oracle_attn_fwd_dropout")
+    return o, lse
+
+
+def _impl_attn_bwd_dropout(lib, q, k, v, do, o, dtype, causal: bool, scale: float, T: int,
+                           seed: int, offset: int):
+    q, k, v, do = _bits(q), _bits(k), _bits(v), _bits(do)
+    B, H, N, d = _shape(q, k, v)
+    o = _given_o(o, q.shape)
+    if o is None:
+        raise ValueError("the dropout backward takes the row term from a given o")
+    dq = np.empty((B, H, N, d), dtype=np.float64)
+    dk = np.empty_like(dq)
+    dv = np.empty_like(dq)
+    _check(lib.oracle_attn_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(o),
+                                       _dtype_code(dtype), B, H, N, d, int(bool(causal)),
+                                       float(scale), int(T), int(seed), int(offset),
+                                       _ptr(dq), _ptr(dk), _ptr(dv)), "oracle_attn_bwd_dropout")
+    return dq, dk, dv
+
+
 _API = ("num_threads", "decode", "softmax_1d", "softmax_online_1d", "attn_fwd",
         "attn_fwd_rows", "attn_probs", "attn_fwd_tiled", "attn_bwd", "attn_bwd_rows",
-        "attn_fwd_masked")
+        "attn_fwd_masked", "philox4x32_10", "dropout_factors", "attn_fwd_dropout",
+        "attn_bwd_dropout")
 
 
 class Oracle:
@@ -335,3 +407,7 @@ attn_fwd_tiled = _module_fn("attn_fwd_tiled")
 attn_bwd = _module_fn("attn_bwd")
 attn_bwd_rows = _module_fn("attn_bwd_rows")
 attn_fwd_masked = _module_fn("attn_fwd_masked")
+philox4x32_10 = _module_fn("philox4x32_10")
+dropout_factors = _module_fn("dropout_factors")
+attn_fwd_dropout = _module_fn("attn_fwd_dropout")
+attn_bwd_dropout = _module_fn("attn_bwd_dropout")

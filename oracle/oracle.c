@@ -706,3 +706,185 @@ int oracle_attn_fwd_masked(const uint16_t *q, const uint16_t *k, const uint16_t 
     free_problem(&p);
     return fail ? -2 : 0;
 }
+
+/* ---- dropout ---------------------------------------------------------------
+ *
+ * The pages list dropout among the operations fused into the attention
+ * kernel and warn that forward and backward must draw the same random
+ * pattern ([P-wmrh] §1.2 kernel fusion, §4.2 problem 3).  Readings (the pages
+ * fix no generator or mapping): the generator is Philox4x32-10 (Salmon,
+ * Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+ * SC 2011), written here from that definition:
+ *   per round, with M0 = 0xD2511F53, M1 = 0xCD9E8D57,
+ *     (hi0, lo0) = M0 * c0,  (hi1, lo1) = M1 * c2   (64-bit products)
+ *     c = (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0)
+ *   and before every round but the first the key gains
+ *     (k0, k1) += (0x9E3779B9, 0xBB67AE85)   (mod 2^32).
+ * Element (b, h, i, j) of the weights P is kept when its byte is below
+ * T = round((1 - p) * 256), where the 16 bytes of one call with
+ *   counter = (i, 2 * (j / 32) + ((j / 4) % 2), b * H + h, offset),
+ *   key     = (seed low 32 bits, seed high 32 bits)
+ * are, little-endian in the output words, the keys
+ *   j' = 32 * (j / 32) + 8 * g + 4 * ((j / 4) % 2) + e  at byte 4 g + e.
+ * Kept weights are scaled by 256 / T, so E[kept weight] is the weight; the
+ * row sum l and lse stay those of the undropped weights (dropout acts after
+ * the softmax).  T = 0 drops everything (o = 0).
+ */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        c0 = hi1 ^ c1 ^ k0;
+        c1 = lo1;
+        c2 = hi0 ^ c3 ^ k1;
+        c3 = lo0;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The byte that decides element (bh, i, j). */
+static unsigned dropout_byte(int64_t bh, int64_t i, int64_t j, uint64_t seed,
+                             uint32_t offset)
+{
+    const uint32_t ctr[4] = {(uint32_t)i, (uint32_t)(2 * (j / 32) + (j / 4) % 2),
+                             (uint32_t)bh, offset};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, key, out);
+    const int64_t jj = j % 32;
+    const int g = (int)(jj / 8), e = (int)(jj % 4);
+    return (out[g] >> (8 * e)) & 0xffu;
+}
+
+/* Keep factor Z_ij: 256 / T if kept, else 0 (T = round((1 - p) 256)). */
+static double dropout_factor(int64_t bh, int64_t i, int64_t j, uint64_t seed,
+                             uint32_t offset, int T)
+{
+    if (T <= 0) return 0.0;
+    return dropout_byte(bh, i, j, seed, offset) < (unsigned)T ? 256.0 / T : 0.0;
+}
+
+/* The keep factors Z of one head-row range, for tests: z[(bh*N + i)*N + j]. */
+int oracle_dropout_factors(int64_t BH, int64_t N, uint64_t seed, uint32_t offset, int T,
+                           double *z)
+{
+    if (T < 0 || T > 256) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < BH * N; ++r)
+        for (int64_t j = 0; j < N; ++j)
+            z[r * N + j] = dropout_factor(r / N, r % N, j, seed, offset, T);
+    return 0;
+}
+
+/* Forward with dropout: o_i = sum_j P_ij Z_ij v_j, lse as without dropout. */
+int oracle_attn_fwd_dropout(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            int dtype, int64_t B, int64_t H, int64_t N, int64_t d,
+                            int causal, double scale, int T, uint64_t seed,
+                            uint32_t offset, double *o, double *lse)
+{
+    if (T < 0 || T > 256) return -1;
+    problem p;
+    int rc = load_problem(&p, q, k, v, dtype, B, H, N, d, causal, scale);
+    if (rc) return rc;
+    const int64_t rows = B * H * N;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < rows; ++r) {
+                const int64_t bh = r / N, i = r % N;
+                const double *qi = p.q + r * d;
+                const double *kh = p.k + bh * N * d, *vh = p.v + bh * N * d;
+                const int64_t nkeys = causal ? i + 1 : N;
+                double m = -INFINITY;
+                for (int64_t j = 0; j < nkeys; ++j) {
+                    double dot = 0.0;
+                    for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
+                    s[j] = scale * dot;
+                    if (s[j] > m) m = s[j];
+                }
+                double l = 0.0;
+                for (int64_t j = 0; j < nkeys; ++j) l += exp(s[j] - m);
+                double *orow = o + r * d;
+                for (int64_t c = 0; c < d; ++c) orow[c] = 0.0;
+                for (int64_t j = 0; j < nkeys; ++j) {
+                    const double w = exp(s[j] - m) / l * dropout_factor(bh, i, j, seed, offset, T);
+                    if (w == 0.0) continue;
+                    for (int64_t c = 0; c < d; ++c) orow[c] += w * vh[j * d + c];
+                }
+                lse[r] = m + log(l);
+            }
+        }
+        free(s);
+    }
+    free_problem(&p);
+    return fail ? -2 : 0;
+}
+
+/* Backward with dropout, the row term from a given 16-bit o (as the kernel
+ * is handed the forward's output):
+ *   dV_j = sum_i P_ij Z_ij dO_i,  dP_ij = dO_i . v_j,
+ *   dS_ij = P_ij (Z_ij dP_ij - D_i),  D_i = dO_i . o_i
+ *   (= sum_j P_ij Z_ij dP_ij for the exact o), dQ, dK as without dropout. */
+int oracle_attn_bwd_dropout(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            const uint16_t *dO, const uint16_t *o, int dtype, int64_t B,
+                            int64_t H, int64_t N, int64_t d, int causal, double scale,
+                            int T, uint64_t seed, uint32_t offset, double *dq, double *dk,
+                            double *dv)
+{
+    if (T < 0 || T > 256 || !o) return -1;
+    bproblem bp;
+    int rc = load_bproblem(&bp, q, k, v, dO, o, dtype, B, H, N, d, causal, scale);
+    if (rc) return rc;
+    const int64_t n = B * H * N * d;
+    for (int64_t t = 0; t < n; ++t) dq[t] = dk[t] = dv[t] = 0.0;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *prow = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        double *dprow = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (!prow || !dprow) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bh = 0; bh < B * H; ++bh) {
+                const double *qh = bp.p.q + bh * N * d, *kh = bp.p.k + bh * N * d;
+                const double *doh = bp.dO + bh * N * d;
+                double *dqh = dq + bh * N * d, *dkh = dk + bh * N * d, *dvh = dv + bh * N * d;
+                for (int64_t i = 0; i < N; ++i) {
+                    /* P_i. and dP_i.; with o given, grad_row returns dO_i . o_i */
+                    const double D = grad_row(&bp, bh, i, prow, dprow, NULL);
+                    const int64_t nkeys = causal ? i + 1 : N;
+                    for (int64_t j = 0; j < nkeys; ++j) {
+                        const double z = dropout_factor(bh, i, j, seed, offset, T);
+                        const double ds = prow[j] * (z * dprow[j] - D);
+                        for (int64_t c = 0; c < d; ++c) {
+                            dqh[i * d + c] += scale * ds * kh[j * d + c];
+                            dkh[j * d + c] += scale * ds * qh[i * d + c];
+                            dvh[j * d + c] += prow[j] * z * doh[i * d + c];
+                        }
+                    }
+                }
+            }
+        }
+        free(prow);
+        free(dprow);
+    }
+    free_bproblem(&bp);
+    return fail ? -2 : 0;
+}

@@ -345,6 +345,79 @@ def pin_masked(orc) -> bool:
     return ok
 
 
+# ---------------------------------------------------------------- dropout
+
+def pin_philox_kat(orc) -> bool:
+    g = json.loads((GOLDEN / "philox4x32_10_kat.json").read_text())
+    ok = True
+    for vec in g["vectors"]:
+        c = [int(x, 16) for x in vec["counter"]]
+        kk = [int(x, 16) for x in vec["key"]]
+        want = [int(x, 16) for x in vec["out"]]
+        ok &= [int(x) for x in orc.philox4x32_10(c, kk)] == want
+    return ok
+
+
+def pin_dropout(orc) -> bool:
+    import oracle as _o
+    ok = True
+    seed, off = 0x0123456789ABCDEF, 7
+    # the mapping: element (bh, i, j) takes byte 4 (j%32 // 8) + j%4 of the call
+    # with counter (i, 2 (j // 32) + (j // 4) % 2, bh, offset)
+    T = _o.dropout_threshold(0.3)
+    z = orc.dropout_factors(3, 70, seed, off, T)
+    key = [seed & 0xffffffff, seed >> 32]
+    want = np.zeros_like(z)
+    for bh in range(3):
+        for i in range(70):
+            for jb in range(3):
+                for hh in range(2):
+                    out = orc.philox4x32_10([i, 2 * jb + hh, bh, off], key)
+                    for g in range(4):
+                        for e in range(4):
+                            j = 32 * jb + 8 * g + 4 * hh + e
+                            if j < 70:
+                                byte = (int(out[g]) >> (8 * e)) & 0xff
+                                want[bh, i, j] = 256.0 / T if byte < T else 0.0
+    ok &= bool(np.array_equal(z, want))
+    # keep rate within 5 sigma of T/256
+    kept = float((z > 0).mean())
+    ok &= abs(kept - T / 256) <= 5 * math.sqrt(T / 256 * (1 - T / 256) / z.size)
+    # p = 0: plain attention; o_i = sum_j P_ij Z_ij v_j against torch fp64
+    q, k, v = _qkv(2, 2, 29, 8, "bf16", seed=22)
+    do = _qkv(2, 2, 29, 8, "bf16", seed=23)[0]
+    for causal in (False, True):
+        o0, l0 = orc.attn_fwd_dropout(bits(q), bits(k), bits(v), "bf16", causal, 0.4, 256, seed, off)
+        ro, rl = orc.attn_fwd(bits(q), bits(k), bits(v), "bf16", causal, 0.4)
+        ok &= _close(o0, ro, 1e-14) and _close(l0, rl, 0.0)
+        o1, l1 = orc.attn_fwd_dropout(bits(q), bits(k), bits(v), "bf16", causal, 0.4, T, seed, off)
+        _, tl, tp = torch_reference(q, k, v, causal, 0.4)
+        Z = orc.dropout_factors(4, 29, seed, off, T).reshape(2, 2, 29, 29)
+        ok &= _close(o1, (tp * Z) @ v.double().numpy(), 1e-12) and _close(l1, tl, 1e-12)
+        # backward: autograd of sum(dO * (softmax(S) o Z) V), shifted by the
+        # given-o row term dD_i = dO_i . (o_i - O_i) exactly as without dropout
+        ro16 = to_tensor(o1, "bf16")
+        g = orc.attn_bwd_dropout(bits(q), bits(k), bits(v), bits(do), bits(ro16), "bf16", causal,
+                                 0.4, T, seed, off)
+        qq, kk2, vv = (t.double().clone().requires_grad_() for t in (q, k, v))
+        sc = torch.matmul(qq, kk2.transpose(-1, -2)) * 0.4
+        if causal:
+            sc = sc.masked_fill(torch.ones(29, 29, dtype=torch.bool).triu(1), float("-inf"))
+        P = torch.softmax(sc, dim=-1)
+        torch.matmul(P * torch.from_numpy(Z), vv).backward(do.double())
+        dD = (do.double().numpy() * (ro16.double().numpy() - o1)).sum(-1)
+        Pn = P.detach().numpy()
+        want_dq = qq.grad.numpy() - 0.4 * dD[..., None] * (Pn @ k.double().numpy())
+        want_dk = kk2.grad.numpy() - 0.4 * (np.swapaxes(Pn, -1, -2) @ (dD[..., None] * q.double().numpy()))
+        ok &= _close(g[0], want_dq, 1e-12) and _close(g[1], want_dk, 1e-12)
+        ok &= _close(g[2], vv.grad.numpy(), 1e-12)
+        g0 = orc.attn_bwd_dropout(bits(q), bits(k), bits(v), bits(do), bits(ro16), "bf16", causal,
+                                  0.4, 256, seed, off)
+        g1 = orc.attn_bwd(bits(q), bits(k), bits(v), bits(do), "bf16", causal, 0.4, o=bits(ro16))
+        ok &= all(_close(a, b, 1e-14) for a, b in zip(g0, g1))
+    return ok
+
+
 PINS = {
     "brute_force": pin_brute_force,
     "python_loops": pin_python_loops,
@@ -361,6 +434,8 @@ PINS = {
     "bwd_rows": pin_bwd_rows,
     "bwd_given_o": pin_bwd_given_o,
     "masked": pin_masked,
+    "philox_kat": pin_philox_kat,
+    "dropout": pin_dropout,
 }
 
 

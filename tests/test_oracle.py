@@ -322,10 +322,15 @@ MUTANTS = [
     ("const double ds = prow[j] * (dprow[j] - D);\n                        for",
      "const double ds = prow[j] * dprow[j];\n                        for",
      "bwd: softmax Jacobian without the row term"),
-    ("dqh[i * d + c] += scale * ds * kh[j * d + c];", "dqh[i * d + c] += ds * kh[j * d + c];",
+    ("dqh[i * d + c] += scale * ds * kh[j * d + c];\n                            dkh[j * d + c] += scale * ds * qh[i * d + c];\n                            dvh[j * d + c] += prow[j] * doh",
+     "dqh[i * d + c] += ds * kh[j * d + c];\n                            dkh[j * d + c] += scale * ds * qh[i * d + c];\n                            dvh[j * d + c] += prow[j] * doh",
      "bwd: dQ without scale"),
-    ("dkh[j * d + c] += scale * ds * qh[i * d + c];",
-     "dkh[j * d + c] += scale * ds * kh[i * d + c];", "bwd: dK from K instead of Q"),
+    ("dkh[j * d + c] += scale * ds * qh[i * d + c];\n                            dvh[j * d + c] += prow[j] * doh",
+     "dkh[j * d + c] += scale * ds * kh[i * d + c];\n                            dvh[j * d + c] += prow[j] * doh",
+     "bwd: dK from K instead of Q"),
+    ("dkh[j * d + c] += scale * ds * qh[i * d + c];\n                            dvh[j * d + c] += prow[j] * z",
+     "dkh[j * d + c] += scale * ds * kh[i * d + c];\n                            dvh[j * d + c] += prow[j] * z",
+     "dropout bwd: dK from K instead of Q"),
     ("dvh[j * d + c] += prow[j] * doh[i * d + c];", "dvh[j * d + c] += prow[j] * doh[j * d + c];",
      "bwd: dV row index"),
     ("D += prow[j] * dp;", "D += dp;", "bwd: row term without P"),
@@ -352,6 +357,18 @@ MUTANTS = [
      "mask: window right edge off by one"),
     ("if (hi > L - 1) hi = L - 1;", "if (hi > N - 1) hi = N - 1;", "mask: window ignores padding"),
     ("if (i >= L || lo > hi) {", "if (lo > hi) {", "mask: padded rows not emptied"),
+    ("            k0 += 0x9E3779B9u;", "            k0 += 0x9E3779B7u;", "philox: key bump constant"),
+    ("        c0 = hi1 ^ c1 ^ k0;", "        c0 = hi0 ^ c1 ^ k0;", "philox: round word order"),
+    ("(uint32_t)(2 * (j / 32) + (j / 4) % 2)", "(uint32_t)(2 * (j / 32))",
+     "dropout: half-lane counter term"),
+    ("return (out[g] >> (8 * e)) & 0xffu;", "return (out[e] >> (8 * g)) & 0xffu;",
+     "dropout: byte index transposed"),
+    ("< (unsigned)T ? 256.0 / T : 0.0;", "<= (unsigned)T ? 256.0 / T : 0.0;",
+     "dropout: keep threshold off by one"),
+    ("const double ds = prow[j] * (z * dprow[j] - D);", "const double ds = prow[j] * (dprow[j] - D);",
+     "dropout bwd: dS without the keep factor"),
+    ("dvh[j * d + c] += prow[j] * z * doh[i * d + c];", "dvh[j * d + c] += prow[j] * doh[i * d + c];",
+     "dropout bwd: dV without the keep factor"),
 ]
 
 
@@ -420,6 +437,30 @@ def test_masked_rejects_bad_lengths(oracle_mod):
     q, k, v = make_qkv(2, 1, 8, 4, "f16", seed=1)
     with pytest.raises(RuntimeError):
         oracle_mod.attn_fwd_masked(bits(q), bits(k), bits(v), "f16", -1, -1, [8, 9], 0.5)
+
+
+# ---------------------------------------------------------------- dropout
+
+@pytest.mark.parametrize("name", ["philox_kat", "dropout"])
+def test_dropout_pins(oracle_mod, name):
+    assert PINS[name](oracle_mod)
+
+
+@pytest.mark.parametrize("p", [0.0, 0.1, 0.5, 0.9, 0.999])
+def test_dropout_threshold(p):
+    import oracle
+    T = oracle.dropout_threshold(p)
+    assert 0 <= T <= 256 and abs(T / 256 - (1 - p)) <= 1 / 512
+
+
+def test_dropout_streams_differ(oracle_mod):
+    """Different seeds or offsets give different patterns; the same give the
+    same (the forward and backward draw one pattern)."""
+    T = 128
+    a = oracle_mod.dropout_factors(2, 64, 1, 0, T)
+    assert np.array_equal(a, oracle_mod.dropout_factors(2, 64, 1, 0, T))
+    for b in (oracle_mod.dropout_factors(2, 64, 2, 0, T), oracle_mod.dropout_factors(2, 64, 1, 1, T)):
+        assert 0.4 < float((a != b).mean()) < 0.6
 
 
 @pytest.fixture(scope="module")
