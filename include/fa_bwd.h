@@ -63,6 +63,25 @@ fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o,
                  void *dv, int B, int H, int N, int d, int causal, float scale,
                  fa_dtype dtype, hipStream_t stream);
 
+/* Backward pass of fa_fwd_dropout: the same gradients for
+ *     o_i = sum_j P_ij Z_ij v_j      (Z the keep factors of fa_fwd_dropout)
+ * namely
+ *     dV_j  = sum_i P_ij Z_ij dO_i
+ *     dS_ij = P_ij (Z_ij (dO_i . v_j) - D_i),   D_i = dO_i . o_i
+ *     dQ_i  = scale * sum_j dS_ij k_j,   dK_j = scale * sum_i dS_ij q_i,
+ * with Z redrawn from (seed, offset, p_drop) exactly as the forward call drew
+ * it ("FlashAttention V2 核心原理与架构设计" §4.2, problem 3: forward and
+ * backward must use one random pattern).  D_i = sum_j P_ij Z_ij (dO_i . v_j)
+ * because o_i is the dropped output.  o and lse are those fa_fwd_dropout
+ * wrote for the same q, k, v, causal, scale, p_drop, seed and offset.
+ * Arguments, layouts and errors as fa_bwd; FA_ERR_INVALID_ARG also for
+ * p_drop outside [0, 1) or NaN. */
+fa_status fa_bwd_dropout(const void *q, const void *k, const void *v, const void *o,
+                         const void *dO, const float *lse, float *ws, void *dq, void *dk,
+                         void *dv, int B, int H, int N, int d, int causal, float scale,
+                         float p_drop, unsigned long long seed, unsigned offset,
+                         fa_dtype dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

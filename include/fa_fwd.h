@@ -124,6 +124,34 @@ fa_status fa_fwd_split(const void *q, const void *k, const void *v, void *o,
                        float scale, int num_splits, float *ws, fa_dtype dtype,
                        hipStream_t stream);
 
+/* Forward pass with dropout on the attention weights, the operation that
+ * "FlashAttention V2 核心原理与架构设计" (wmrh.cn) fuses into the kernel
+ * (§1.2, with a dropout_p argument in §5.2) and whose random pattern must be
+ * the same in the forward and the backward pass (§4.2, problem 3).  The page
+ * fixes no generator, mapping or scaling; this library uses:
+ *     T    = floor((1 - p_drop) * 256 + 0.5), computed in double from the
+ *            float p_drop
+ *     keep element (b,h,i,j) iff byte 4*((j%32)/8) + j%4 (little-endian
+ *            across the four output words) of Philox4x32-10 (Salmon et al.,
+ *            SC 2011) with
+ *              counter = (i, 2*(j/32) + (j/4)%2, b*H + h, offset)
+ *              key     = (seed & 0xffffffff, seed >> 32)
+ *            is below T
+ *     o[b,h,i,:] = sum_j P_ij * Z_ij * v[b,h,j,:],  Z_ij = 256/T if kept,
+ *            else 0 (every Z = 0 when T = 0)
+ *     lse   unchanged: that of the undropped weights P.
+ * A call with the same seed and offset draws the same pattern (the same
+ * bits, on any stream or grid); fa_bwd_dropout redraws it.  Advancing the
+ * offset (or the seed) between training steps gives fresh patterns.
+ *   causal   0 or 1, as fa_fwd
+ *   p_drop   dropout probability, 0 <= p_drop < 1 (p_drop = 0 keeps all)
+ * Other arguments, layouts and errors as fa_fwd; FA_ERR_INVALID_ARG also for
+ * p_drop outside [0, 1) or NaN. */
+fa_status fa_fwd_dropout(const void *q, const void *k, const void *v, void *o,
+                         float *lse, int B, int H, int N, int d, int causal,
+                         float scale, float p_drop, unsigned long long seed,
+                         unsigned offset, fa_dtype dtype, hipStream_t stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *fa_status_string(int status);
 

@@ -18,6 +18,10 @@ C entry points mirrored here with the same names and argument order:
   fa_bwd(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale,
          dtype, stream) -> status
   fa_bwd_workspace_size(B, H, N) -> bytes
+  fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, causal, scale, p_drop, seed, offset,
+                 dtype, stream) -> status
+  fa_bwd_dropout(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale,
+                 p_drop, seed, offset, dtype, stream) -> status
   fa_status_string(status) -> str
 Pointers may be given as integers or as tensors (their data_ptr()); the
 stream as an integer handle, a torch.cuda.Stream, or None (null stream).
@@ -39,7 +43,7 @@ FA_DTYPE_BF16 = 1
 
 EXPORTED = ("fa_fwd_f16", "fa_fwd_bf16", "fa_fwd", "fa_fwd_window", "fa_fwd_split",
             "fa_fwd_split_workspace_size", "fa_status_string", "fa_bwd",
-            "fa_bwd_workspace_size")
+            "fa_bwd_workspace_size", "fa_fwd_dropout", "fa_bwd_dropout")
 FA_MAX_SPLITS = 64
 
 _lib = None
@@ -84,6 +88,12 @@ def load():
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd_workspace_size.argtypes = [i, i, i]
     lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    u64 = ctypes.c_ulonglong
+    u32 = ctypes.c_uint
+    lib.fa_fwd_dropout.argtypes = sig + [f, u64, u32, i, p]
+    lib.fa_fwd_dropout.restype = ctypes.c_int
+    lib.fa_bwd_dropout.argtypes = [p] * 10 + [i, i, i, i, i, f, f, u64, u32, i, p]
+    lib.fa_bwd_dropout.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -148,6 +158,22 @@ def fa_bwd(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale, dtype
 
 def fa_bwd_workspace_size(B, H, N) -> int:
     return int(load().fa_bwd_workspace_size(int(B), int(H), int(N)))
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, causal, scale, p_drop, seed, offset, dtype,
+                   stream=None) -> int:
+    return load().fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B),
+                                 int(H), int(N), int(d), int(causal), float(scale),
+                                 float(p_drop), int(seed), int(offset), int(dtype),
+                                 _stream(stream))
+
+
+def fa_bwd_dropout(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale, p_drop,
+                   seed, offset, dtype, stream=None) -> int:
+    return load().fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+                                 _ptr(ws), _ptr(dq), _ptr(dk), _ptr(dv), int(B), int(H),
+                                 int(N), int(d), int(causal), float(scale), float(p_drop),
+                                 int(seed), int(offset), int(dtype), _stream(stream))
 
 
 def fa_status_string(status: int) -> str:

@@ -130,6 +130,58 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int byt
     return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, bytes, kRsrcWord3);
 }
 
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011): ten rounds of two
+// 32x32 -> 64-bit products (multipliers 0xD2511F53 on word 0, 0xCD9E8D57 on
+// word 2), high halves XORed with the other words and the key, the key
+// bumped by (0x9E3779B9, 0xBB67AE85) between rounds.
+__device__ __forceinline__ u32x4 philox4x32_10(unsigned c0, unsigned c1, unsigned c2,
+                                               unsigned c3, unsigned k0, unsigned k1)
+{
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const unsigned long long a = (unsigned long long)0xD2511F53u * c0;
+        const unsigned long long b = (unsigned long long)0xCD9E8D57u * c2;
+        const unsigned n0 = (unsigned)(b >> 32) ^ c1 ^ k0;
+        const unsigned n2 = (unsigned)(a >> 32) ^ c3 ^ k1;
+        c1 = (unsigned)b;
+        c3 = (unsigned)a;
+        c0 = n0;
+        c2 = n2;
+    }
+    const u32x4 r = {c0, c1, c2, c3};
+    return r;
+}
+
+// Dropout parameters of one launch (as the forward pass): a weight is kept
+// when its random byte is below thr; kept weights are scaled by fscale.
+struct DropArgs {
+    unsigned seed_lo, seed_hi, offset, thr;
+    float fscale;
+};
+
+// Byte transpose of a 4x4 byte matrix held by the 4 lanes of a quad (lane e
+// holds row e as one word): afterwards lane e holds column e.  Two stages:
+// swap 16-bit halves with lane e^2, then bytes with lane e^1 (DPP quad
+// permutes, v_perm_b32 with a per-lane selector).
+struct QuadTranspose {
+    unsigned sel1, sel2;
+    __device__ __forceinline__ explicit QuadTranspose(int lane) {
+        // v_perm_b32(a, b, sel): selector byte 0-3 takes a byte of b, 4-7 of a
+        sel1 = (lane & 2) ? 0x07060302u : 0x01000504u;   // [y2 y3 x2 x3] : [x0 x1 y0 y1]
+        sel2 = (lane & 1) ? 0x07030501u : 0x02060004u;   // [y1 x1 y3 x3] : [x0 y0 x2 y2]
+    }
+    __device__ __forceinline__ unsigned operator()(unsigned x) const {
+        const unsigned y = (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
+        const unsigned z = __builtin_amdgcn_perm(x, y, sel1);
+        const unsigned w = (unsigned)__builtin_amdgcn_mov_dpp((int)z, 0xB1, 0xF, 0xF, false);
+        return __builtin_amdgcn_perm(z, w, sel2);
+    }
+};
+
 // One 1 KB HBM -> LDS load of rows [row0, row0 + 1024 / (2 d)) of a swizzled
 // [rows, d] tile: lane l lands at dst + 16 l, which is (row, physical chunk
 // l % (d / 8)), so it fetches the logical chunk that belongs there.
@@ -184,12 +236,19 @@ void fa_bwd_delta_kernel(const u16 *__restrict__ O, const u16 *__restrict__ dO,
 
 // ---------------------------------------------------------------- dK / dV
 
-template <int DT, int D, bool CAUSAL>
+// DROP: the dropout of the forward pass, redrawn.  dV^T += dO^T (P o Z) and
+// dS = P o (Z o dP - D).  A lane here holds one key and 16 queries, while a
+// Philox call yields 16 keys of one query, so each lane makes the call of
+// (query qs + l32, key half hh) of the step and the 32 x 32 bytes are
+// transposed through a per-wave 1 KB LDS block: a byte transpose inside each
+// lane quad, 4 dword writes, one 16-byte read per lane.
+template <int DT, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                         const u16 *__restrict__ V, const u16 *__restrict__ dO,
                         const float *__restrict__ WS, u16 *__restrict__ dK,
-                        u16 *__restrict__ dV, int BH, int N, int nblk, float c2, float scale)
+                        u16 *__restrict__ dV, int BH, int N, int nblk, float c2, float scale,
+                        DropArgs dr)
 {
     using E = Elem<DT>;
     using T = Tile<D>;
@@ -206,6 +265,8 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     __shared__ __attribute__((aligned(1024))) unsigned char o1s[QTB];
     __shared__ __attribute__((aligned(256))) float w0s[2 * kQT];
     __shared__ __attribute__((aligned(256))) float w1s[2 * kQT];
+    // dropout bytes of one step, per wave: [key 32][query half 2][g 4] words
+    __shared__ __attribute__((aligned(1024))) unsigned zs[DROP ? kWaves * 256 : 1];
     auto qbuf = [&](auto b) -> LDS unsigned char * {
         if constexpr (decltype(b)::value == 0) return (LDS unsigned char *)q0s;
         else return (LDS unsigned char *)q1s;
@@ -315,11 +376,34 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 #pragma unroll
         for (int r = 0; r < 16; ++r) dva[db][r] = dka[db][r] = 0.f;
 
+    // Dropout bytes of step qs, as lane (key kw + l32, query half hh) needs
+    // them: word g, byte e is query qs + 8g + 4hh + e (the accumulator row of
+    // register 4g + e).  Lane (query m = l32, key half hh) draws the call for
+    // query qs + m; its word gk, byte ek is key 8gk + 4hh + ek.  After the
+    // quad transpose, word gk of lane (quad a = m/4, position e = m%4) holds,
+    // for key 8gk + 4hh + e, the four queries 4a..4a+3: word a/2 of query
+    // half a%2.
+    LDS unsigned *zw = (LDS unsigned *)zs + (DROP ? 256 * w : 0);
+    const QuadTranspose qtr(lane);
+    auto drop_bytes = [&](int qs) -> u32x4 {
+        const u32x4 r = philox4x32_10((unsigned)(qs + l32), (unsigned)(2 * (kw / 32) + hh),
+                                      (unsigned)bh, dr.offset, dr.seed_lo, dr.seed_hi);
+        const int a = l32 >> 2, e = l32 & 3;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int gk = 0; gk < 4; ++gk)
+            zw[(8 * gk + 4 * hh + e) * 8 + (a & 1) * 4 + (a >> 1)] = qtr(r[gk]);
+        __builtin_amdgcn_wave_barrier();
+        const u32x4 z = *(const LDS u32x4 *)(zw + l32 * 8 + hh * 4);
+        __builtin_amdgcn_wave_barrier();
+        return z;
+    };
+
     // one step: 32 queries (sub-step u of the tile in buffers par).  Every
     // MFMA loop reads its LDS operands a fixed distance ahead, and the
     // interleave is pinned (scheduling-group barriers) so that neither the
     // reads crowd the registers nor each MFMA waits on its own read.
-    auto step = [&](auto par, int u, bool diag) {
+    auto step = [&](auto par, int u, bool diag, int qs) {
         LDS unsigned char *qb = qbuf(par);
         LDS unsigned char *ob = obuf(par);
         LDS float *wb = wbuf(par) + u * 2 * kWsRows;
@@ -345,12 +429,17 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             __builtin_amdgcn_sched_barrier(0);
         }
         // dP' = dO V^T - D: the accumulator starts at -D of the lane's rows
+        // (at 0 under dropout, where D enters after the keep factor)
         f32x16 dp;
+        if constexpr (DROP) {
+            dp = f32x16{};
+        } else {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const f32x4 dv4 = *(const LDS f32x4 *)(wb + kWsRows + 8 * g + 4 * hh);
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 dv4 = *(const LDS f32x4 *)(wb + kWsRows + 8 * g + 4 * hh);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dp[4 * g + e] = -dv4[e];
+                for (int e = 0; e < 4; ++e) dp[4 * g + e] = -dv4[e];
+            }
         }
         {
             constexpr int AH = 2;
@@ -379,17 +468,28 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             __builtin_amdgcn_sched_barrier(0);
         }
         // P = 2^(S c2 - lse log2 e), dS = P dP'; rows m = 8(r/4) + 4hh + r%4
+        u32x4 zb;
+        if constexpr (DROP) zb = drop_bytes(qs);
         u32x4 pp[2], dsp[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x4 l4 = *(const LDS f32x4 *)(wb + 8 * g + 4 * hh);
+            f32x4 d4;
+            if constexpr (DROP) d4 = *(const LDS f32x4 *)(wb + kWsRows + 8 * g + 4 * hh);
             float p[4], ds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float x = fmaf(s[4 * g + e], c2, -l4[e]);
                 if (diag && l32 > 8 * g + 4 * hh + e) x = neg_inf();
                 p[e] = __builtin_amdgcn_exp2f(x);
-                ds[e] = p[e] * dp[4 * g + e];
+                if constexpr (DROP) {
+                    // dS = P (Z dP - D), and P Z for the dV product
+                    const float zf = ((zb[g] >> (8 * e)) & 0xffu) < dr.thr ? dr.fscale : 0.f;
+                    ds[e] = p[e] * fmaf(zf, dp[4 * g + e], -d4[e]);
+                    p[e] *= zf;
+                } else {
+                    ds[e] = p[e] * dp[4 * g + e];
+                }
             }
             pp[g >> 1][2 * (g & 1)] = E::pack2(p[0], p[1]);
             pp[g >> 1][2 * (g & 1) + 1] = E::pack2(p[2], p[3]);
@@ -433,7 +533,7 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 #pragma unroll
         for (int u = 0; u < kQT / 32; ++u) {
             const int qs = t * kQT + 32 * u;   // first query of the step
-            if (!CAUSAL || qs + 31 >= kw) step(par, u, CAUSAL && qs == kw);
+            if (!CAUSAL || qs + 31 >= kw) step(par, u, CAUSAL && qs == kw, qs);
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_waitcnt(0);
@@ -469,12 +569,14 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
 // ---------------------------------------------------------------- dQ
 
-template <int DT, int D, bool CAUSAL>
+// DROP: dS = P o (Z o dP - D) with the forward's keep factors Z; a lane
+// holds 16 keys of one query, the 16 bytes of one Philox call per step.
+template <int DT, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                       const u16 *__restrict__ V, const u16 *__restrict__ dO,
                       const float *__restrict__ WS, u16 *__restrict__ dQ, int BH, int N,
-                      int nblk, int nqb, float c2, float scale)
+                      int nblk, int nqb, float c2, float scale, DropArgs dr)
 {
     using E = Elem<DT>;
     using T = Tile<D>;
@@ -590,10 +692,15 @@ void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         for (int kk = 0; kk < KT; ++kk) s = E::mfma(rfrag(kb, u, kk), qf[kk], s);
         f32x16 dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = -dd;
+        for (int r = 0; r < 16; ++r) dp[r] = DROP ? 0.f : -dd;
 #pragma unroll
         for (int kk = 0; kk < KT; ++kk) dp = E::mfma(rfrag(vb, u, kk), of[kk], dp);
-        // rows = keys ks0 + 8(r/4) + 4hh + r%4, column = query qrow
+        // rows = keys ks0 + 8(r/4) + 4hh + r%4, column = query qrow; under
+        // dropout register 4g + e is byte 4g + e of the step's call
+        u32x4 zb;
+        if constexpr (DROP)
+            zb = philox4x32_10((unsigned)qrow, (unsigned)(2 * (ks0 / 32) + hh), (unsigned)bh,
+                               dr.offset, dr.seed_lo, dr.seed_hi);
         u32x4 dsp[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -602,7 +709,12 @@ void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             for (int e = 0; e < 4; ++e) {
                 float x = fmaf(s[4 * g + e], c2, -l2);
                 if (diag && ks0 + 8 * g + 4 * hh + e > qrow) x = neg_inf();
-                ds[e] = __builtin_amdgcn_exp2f(x) * dp[4 * g + e];
+                if constexpr (DROP) {
+                    const float zf = ((zb[g] >> (8 * e)) & 0xffu) < dr.thr ? dr.fscale : 0.f;
+                    ds[e] = __builtin_amdgcn_exp2f(x) * fmaf(zf, dp[4 * g + e], -dd);
+                } else {
+                    ds[e] = __builtin_amdgcn_exp2f(x) * dp[4 * g + e];
+                }
             }
             dsp[g >> 1][2 * (g & 1)] = E::pack2(ds[0], ds[1]);
             dsp[g >> 1][2 * (g & 1) + 1] = E::pack2(ds[2], ds[3]);
@@ -657,10 +769,10 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
     return x < y + nb && y < x + na;
 }
 
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, bool DROP>
 hipError_t launch(const void *q, const void *k, const void *v, const void *o, const void *dO,
                   const float *lse, float *ws, void *dq, void *dk, void *dv, int BH, int N,
-                  float scale, hipStream_t stream)
+                  float scale, DropArgs dr, hipStream_t stream)
 {
     const int nblk = (N + kWsRows - 1) / kWsRows;
     const long long rows_padded = (long long)BH * nblk * kWsRows;
@@ -671,27 +783,34 @@ hipError_t launch(const void *q, const void *k, const void *v, const void *o, co
     const float c2 = scale * kLog2e;
     hipLaunchKernelGGL((fa_bwd_delta_kernel<DT, D>), dim3((unsigned)g1), dim3(256), 0, stream,
                        (const u16 *)o, (const u16 *)dO, lse, ws, N, nblk, rows_padded);
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)((long long)BH * nkb)),
-                       dim3(kThreads), 0, stream, (const u16 *)q, (const u16 *)k,
-                       (const u16 *)v, (const u16 *)dO, (const float *)ws, (u16 *)dk,
-                       (u16 *)dv, BH, N, nblk, c2, scale);
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<DT, D, CAUSAL>), dim3((unsigned)((long long)BH * nqb)),
-                       dim3(kThreads), 0, stream, (const u16 *)q, (const u16 *)k,
-                       (const u16 *)v, (const u16 *)dO, (const float *)ws, (u16 *)dq, BH, N,
-                       nblk, nqb, c2, scale);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D, CAUSAL, DROP>),
+                       dim3((unsigned)((long long)BH * nkb)), dim3(kThreads), 0, stream,
+                       (const u16 *)q, (const u16 *)k, (const u16 *)v, (const u16 *)dO,
+                       (const float *)ws, (u16 *)dk, (u16 *)dv, BH, N, nblk, c2, scale, dr);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<DT, D, CAUSAL, DROP>),
+                       dim3((unsigned)((long long)BH * nqb)), dim3(kThreads), 0, stream,
+                       (const u16 *)q, (const u16 *)k, (const u16 *)v, (const u16 *)dO,
+                       (const float *)ws, (u16 *)dq, BH, N, nblk, nqb, c2, scale, dr);
     return hipGetLastError();
 }
 
 typedef hipError_t (*launch_fn)(const void *, const void *, const void *, const void *,
                                 const void *, const float *, float *, void *, void *, void *,
-                                int, int, float, hipStream_t);
+                                int, int, float, DropArgs, hipStream_t);
+
+template <int DT, bool DROP>
+launch_fn pick_drop(int d, int causal)
+{
+    if (d == 64) return causal ? launch<DT, 64, true, DROP> : launch<DT, 64, false, DROP>;
+    return causal ? launch<DT, 128, true, DROP> : launch<DT, 128, false, DROP>;
+}
 
 template <int DT>
-launch_fn pick(int d, int causal)
+launch_fn pick(int d, int causal, bool drop)
 {
-    if (d == 64) return causal ? launch<DT, 64, true> : launch<DT, 64, false>;
-    return causal ? launch<DT, 128, true> : launch<DT, 128, false>;
+    return drop ? pick_drop<DT, true>(d, causal) : pick_drop<DT, false>(d, causal);
 }
+
 
 }  // namespace
 
@@ -701,10 +820,13 @@ extern "C" size_t fa_bwd_workspace_size(int B, int H, int N)
     return (size_t)B * (size_t)H * (size_t)((N + kWsRows - 1) / kWsRows) * 2 * kWsRows * sizeof(float);
 }
 
-extern "C" fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o,
-                            const void *dO, const float *lse, float *ws, void *dq, void *dk,
-                            void *dv, int B, int H, int N, int d, int causal, float scale,
-                            fa_dtype dtype, hipStream_t stream)
+namespace {
+
+// Validation and launch shared by fa_bwd and fa_bwd_dropout.
+fa_status run_bwd(const void *q, const void *k, const void *v, const void *o, const void *dO,
+                  const float *lse, float *ws, void *dq, void *dk, void *dv, int B, int H,
+                  int N, int d, int causal, float scale, fa_dtype dtype, const DropArgs *drop,
+                  hipStream_t stream)
 {
     if (!q || !k || !v || !o || !dO || !lse || !ws || !dq || !dk || !dv)
         return FA_ERR_INVALID_ARG;
@@ -740,9 +862,35 @@ extern "C" fa_status fa_bwd(const void *q, const void *k, const void *v, const v
             if (overlaps(outs[a], outsz[a], outs[b], outsz[b])) return FA_ERR_INVALID_ARG;
     }
 
-    launch_fn fn = (dtype == FA_DTYPE_F16) ? pick<FA_DTYPE_F16>(d, causal)
-                                           : pick<FA_DTYPE_BF16>(d, causal);
-    if (fn(q, k, v, o, dO, lse, ws, dq, dk, dv, (int)BH, N, scale, stream) != hipSuccess)
+    launch_fn fn = (dtype == FA_DTYPE_F16) ? pick<FA_DTYPE_F16>(d, causal, drop != nullptr)
+                                           : pick<FA_DTYPE_BF16>(d, causal, drop != nullptr);
+    const DropArgs dr = drop ? *drop : DropArgs{0u, 0u, 0u, 256u, 1.f};
+    if (fn(q, k, v, o, dO, lse, ws, dq, dk, dv, (int)BH, N, scale, dr, stream) != hipSuccess)
         return FA_ERR_LAUNCH;
     return FA_OK;
+}
+
+}  // namespace
+
+extern "C" fa_status fa_bwd(const void *q, const void *k, const void *v, const void *o,
+                            const void *dO, const float *lse, float *ws, void *dq, void *dk,
+                            void *dv, int B, int H, int N, int d, int causal, float scale,
+                            fa_dtype dtype, hipStream_t stream)
+{
+    return run_bwd(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale, dtype,
+                   nullptr, stream);
+}
+
+extern "C" fa_status fa_bwd_dropout(const void *q, const void *k, const void *v, const void *o,
+                                    const void *dO, const float *lse, float *ws, void *dq,
+                                    void *dk, void *dv, int B, int H, int N, int d, int causal,
+                                    float scale, float p_drop, unsigned long long seed,
+                                    unsigned offset, fa_dtype dtype, hipStream_t stream)
+{
+    if (!(p_drop >= 0.f && p_drop < 1.f)) return FA_ERR_INVALID_ARG;
+    const unsigned thr = (unsigned)floor((1.0 - (double)p_drop) * 256.0 + 0.5);
+    const DropArgs dr = {(unsigned)seed, (unsigned)(seed >> 32), offset, thr,
+                         thr ? 256.f / (float)thr : 0.f};
+    return run_bwd(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale, dtype, &dr,
+                   stream);
 }

@@ -204,6 +204,41 @@ __device__ __forceinline__ float half_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds of two 32x32 -> 64-bit products
+// with the multipliers 0xD2511F53 (word 0) and 0xCD9E8D57 (word 2), the high
+// halves XORed with the other words and the key, the key bumped by the Weyl
+// constants (0x9E3779B9, 0xBB67AE85) between rounds.  The key is uniform
+// over the grid, so its schedule stays in scalar registers.
+__device__ __forceinline__ u32x4 philox4x32_10(unsigned c0, unsigned c1, unsigned c2,
+                                               unsigned c3, unsigned k0, unsigned k1)
+{
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const unsigned long long a = (unsigned long long)0xD2511F53u * c0;
+        const unsigned long long b = (unsigned long long)0xCD9E8D57u * c2;
+        const unsigned n0 = (unsigned)(b >> 32) ^ c1 ^ k0;
+        const unsigned n2 = (unsigned)(a >> 32) ^ c3 ^ k1;
+        c1 = (unsigned)b;
+        c3 = (unsigned)a;
+        c0 = n0;
+        c2 = n2;
+    }
+    const u32x4 r = {c0, c1, c2, c3};
+    return r;
+}
+
+// Dropout parameters of one launch: a weight is kept when its random byte is
+// below thr, and the kept weights are scaled by fscale = 256 / thr.
+struct DropArgs {
+    unsigned seed_lo, seed_hi, offset, thr;
+    float fscale;
+};
+
 // MODE 0: every key; 1: causal (key <= query); 2: window and valid lengths,
 // key j allowed for query i of batch element b when
 // max(0, i - wl) <= j <= min(L_b - 1, i + wr) (wl / wr < 0: that side open;
@@ -213,18 +248,31 @@ __device__ __forceinline__ float half_sum(float x) {
 // normalised O in fp32 to PO and its lse to PL ([y][b*H+h][row]), rows
 // without keys in the segment 0 and -inf, for a merge kernel to combine.
 // Modes 0 and 1 ignore H, wl, wr, LENS, kseg, PO, PL.
-template <int DT, int D, int MODE>
+//
+// DROP (modes 0 and 1 only): dropout on the normalised weights.  Weight
+// (b*H+h, i, j) is kept when byte 4*((j%32)/8) + j%4 of Philox4x32-10 with
+// counter (i, 2*(j/32) + (j/4)%2, b*H+h, offset) and key (seed low word,
+// seed high word) is below dr.thr; kept weights are scaled by dr.fscale.
+// The row sum and lse are those of the undropped weights.  In the MFMA
+// layout a lane's 16 keys of one 32-key block are exactly the 16 bytes of
+// one call (key 8g + 4hh + e is byte 4g + e), so a lane makes one call per
+// 32 keys and no random number is shared between lanes.
+template <int DT, int D, int MODE, bool DROP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                    const u16 *__restrict__ V, u16 *__restrict__ O,
                    float *__restrict__ LSE, int BH, int N, int nqb, float c,
                    unsigned qand, unsigned qxor, int H, int wl, int wr,
                    const int *__restrict__ LENS, int kseg, float *__restrict__ PO,
-                   float *__restrict__ PL)
+                   float *__restrict__ PL, DropArgs dr)
 {
+    static_assert(!DROP || MODE <= 1, "dropout is built for the full and causal masks");
     constexpr bool CAUSAL = MODE == 1;
     constexpr bool GEN = MODE >= 2;
     constexpr bool SPLIT = MODE == 3;
+    // the fp32 row sum is kept for bfloat16 and under dropout (where the
+    // weights applied to V no longer sum to the normaliser)
+    constexpr bool FSUM = DT == FA_DTYPE_BF16 || DROP;
     using E = Elem<DT>;
     using T = Tile<D>;
     constexpr int KT = D / 16;    // MFMA k-steps over d
@@ -462,8 +510,8 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             const float mn = fmaxf(m, mt);
             const float mu = (mn == neg_inf()) ? 0.f : mn;
             const float alpha = __builtin_amdgcn_exp2f(m - mu);
-            if constexpr (DT == FA_DTYPE_BF16) l *= alpha;
-            lh *= alpha;
+            if constexpr (FSUM) l *= alpha;
+            if constexpr (!DROP) lh *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -478,9 +526,17 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     // cancels).  lse uses the fp32 sum for bfloat16; for binary16 the
     // rounded sum is within 2^-11 relative of it (|lse error| <= 4.9e-4),
     // so it serves for both.
-    auto softmax = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PT]) {
+    auto softmax = [&](f32x16 (&s)[NKB], u32x4 (&pk)[PT], int j) {
         const float mu = (m == neg_inf()) ? 0.f : m;
         float rs[4], rh[4];
+        // dropout bytes: one Philox call per 32-key block (see DROP above)
+        u32x4 rnd[NKB];
+        if constexpr (DROP) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                rnd[kb] = philox4x32_10((unsigned)qrow, (unsigned)(2 * (j * NKB + kb) + hh),
+                                        (unsigned)bh, dr.offset, dr.seed_lo, dr.seed_hi);
+        }
         // groups of 8 scores: 8 FMAs, 8 exps, then sums and packing, so the
         // temporaries die inside the group (scheduling barrier per group)
 #pragma unroll
@@ -493,18 +549,30 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(x[e]);
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                if constexpr (DT == FA_DTYPE_BF16) {
+                if constexpr (FSUM) {
                     const float a = p[2 * h] + p[2 * h + 1];
                     rs[h] = (g == 0) ? a : rs[h] + a;
                 }
-                const unsigned pr = E::pack2(p[2 * h], p[2 * h + 1]);
-                rh[h] = E::sum2(pr, (g == 0) ? 0.f : rh[h]);
-                pk[2 * kb + (r0 >> 3)][h] = pr;
+                if constexpr (DROP) {
+                    // register r holds key 8(r/4) + 4hh + r%4: byte r of the call
+                    float z[2];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const int r = r0 + 2 * h + t;
+                        const unsigned byte = (rnd[kb][r >> 2] >> (8 * (r & 3))) & 0xffu;
+                        z[t] = byte < dr.thr ? p[2 * h + t] : 0.f;
+                    }
+                    pk[2 * kb + (r0 >> 3)][h] = E::pack2(z[0], z[1]);
+                } else {
+                    const unsigned pr = E::pack2(p[2 * h], p[2 * h + 1]);
+                    rh[h] = E::sum2(pr, (g == 0) ? 0.f : rh[h]);
+                    pk[2 * kb + (r0 >> 3)][h] = pr;
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (DT == FA_DTYPE_BF16) l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-        lh += (rh[0] + rh[1]) + (rh[2] + rh[3]);
+        if constexpr (FSUM) l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        if constexpr (!DROP) lh += (rh[0] + rh[1]) + (rh[2] + rh[3]);
     };
 
     // O^T += V_j^T P(j)^T, operand i (k-step i / DB, d block i % DB) read
@@ -578,7 +646,7 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                 __builtin_amdgcn_s_setprio(0);
                 if (tile_masked(j)) mask(sc, j);
                 update_max(sc);
-                softmax(sc, pk);
+                softmax(sc, pk, j);
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_setprio(2);
                 pv(Buf<2 + P>{}, pk);
@@ -631,10 +699,12 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         return;
     }
     if (GEN ? (q0 < len) : (n_w > 0)) {
-        const float lht = half_sum(lh);
-        const float lt = (DT == FA_DTYPE_BF16) ? half_sum(l) : lht;
+        // under dropout O is the kept weights' sum scaled by fscale over the
+        // undropped fp32 row sum; otherwise over the rounded-weight sum
+        const float lht = DROP ? 0.f : half_sum(lh);
+        const float lt = FSUM ? half_sum(l) : lht;
         if (GEN ? (qrow < len) : (qrow < N)) {
-            const float inv = 1.f / lht;
+            const float inv = DROP ? dr.fscale / lt : 1.f / lht;
             u16 *orow = O + head + (size_t)qrow * D;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
@@ -653,23 +723,24 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
 typedef void (*kernel_fn)(const u16 *, const u16 *, const u16 *, u16 *, float *,
                           int, int, int, float, unsigned, unsigned, int, int, int,
-                          const int *, int, float *, float *);
+                          const int *, int, float *, float *, DropArgs);
 
 template <int DT, int D>
-kernel_fn pick_d(int mode)
+kernel_fn pick_d(int mode, bool drop)
 {
+    if (drop) return mode == 1 ? fa_fwd_kernel<DT, D, 1, true> : fa_fwd_kernel<DT, D, 0, true>;
     switch (mode) {
-    case 0: return fa_fwd_kernel<DT, D, 0>;
-    case 1: return fa_fwd_kernel<DT, D, 1>;
-    case 2: return fa_fwd_kernel<DT, D, 2>;
-    default: return fa_fwd_kernel<DT, D, 3>;
+    case 0: return fa_fwd_kernel<DT, D, 0, false>;
+    case 1: return fa_fwd_kernel<DT, D, 1, false>;
+    case 2: return fa_fwd_kernel<DT, D, 2, false>;
+    default: return fa_fwd_kernel<DT, D, 3, false>;
     }
 }
 
 template <int DT>
-kernel_fn pick(int d, int mode)
+kernel_fn pick(int d, int mode, bool drop)
 {
-    return d == 64 ? pick_d<DT, 64>(mode) : pick_d<DT, 128>(mode);
+    return d == 64 ? pick_d<DT, 64>(mode, drop) : pick_d<DT, 128>(mode, drop);
 }
 
 // Merge of the key segments of mode 3, per row ([P-baidu] §4.2-§4.3 and the
@@ -757,15 +828,17 @@ fa_status validate_fwd(const void *q, const void *k, const void *v, void *o, flo
 fa_status launch_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B,
                      int H, int N, int d, int mode, int wl, int wr, const int *lens,
                      float scale, fa_dtype dtype, hipStream_t stream, int nseg = 1,
-                     int kseg = 0, float *po = nullptr, float *pl = nullptr)
+                     int kseg = 0, float *po = nullptr, float *pl = nullptr,
+                     const DropArgs *drop = nullptr)
 {
     const fa_status vs = validate_fwd(q, k, v, o, lse, B, H, N, d, lens, scale, dtype);
     if (vs != FA_OK) return vs;
     const long long BH = (long long)B * H;
     const long long nqb = (N + kBR - 1) / kBR;
     const long long grid = BH * nqb;
-    kernel_fn fn = (dtype == FA_DTYPE_F16) ? pick<FA_DTYPE_F16>(d, mode)
-                                           : pick<FA_DTYPE_BF16>(d, mode);
+    if (drop && mode > 1) return FA_ERR_INVALID_ARG;
+    kernel_fn fn = (dtype == FA_DTYPE_F16) ? pick<FA_DTYPE_F16>(d, mode, drop != nullptr)
+                                           : pick<FA_DTYPE_BF16>(d, mode, drop != nullptr);
     // Scores are always taken with a positive multiplier c: scale < 0 negates
     // Q exactly (sign bits) and scale == 0 zeroes Q (every score 0, every
     // allowed key weighted equally); c = |scale| log2(e), or log2(e) for 0.
@@ -779,8 +852,9 @@ fa_status launch_fwd(const void *q, const void *k, const void *v, void *o, float
     void *op = o;
     float *lp = lse, *pop = po, *plp = pl;
     const int *lensp = lens;
+    DropArgs dr = drop ? *drop : DropArgs{0u, 0u, 0u, 256u, 1.f};
     void *args[] = {&qp, &kp, &vp, &op, &lp, &bh_i, &n_i, &nqb_i, &c, &qand, &qxor,
-                    &h_i, &wl_i, &wr_i, &lensp, &kseg_i, &pop, &plp};
+                    &h_i, &wl_i, &wr_i, &lensp, &kseg_i, &pop, &plp, &dr};
     hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)grid, (unsigned)nseg),
                                    dim3(kThreads), args, 0, stream);
     if (e != hipSuccess) return FA_ERR_LAUNCH;
@@ -873,6 +947,20 @@ extern "C" fa_status fa_fwd_split(const void *q, const void *k, const void *v, v
     float *pl = ws + (size_t)nseg * B * H * N * d;
     return launch_fwd(q, k, v, o, lse, B, H, N, d, 3, -1, causal ? 0 : -1, nullptr, scale,
                       dtype, stream, nseg, kseg, po, pl);
+}
+
+extern "C" fa_status fa_fwd_dropout(const void *q, const void *k, const void *v, void *o,
+                                    float *lse, int B, int H, int N, int d, int causal,
+                                    float scale, float p_drop, unsigned long long seed,
+                                    unsigned offset, fa_dtype dtype, hipStream_t stream)
+{
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!(p_drop >= 0.f && p_drop < 1.f)) return FA_ERR_INVALID_ARG;
+    const unsigned thr = (unsigned)floor((1.0 - (double)p_drop) * 256.0 + 0.5);
+    const DropArgs dr = {(unsigned)seed, (unsigned)(seed >> 32), offset, thr,
+                         thr ? 256.f / (float)thr : 0.f};
+    return launch_fwd(q, k, v, o, lse, B, H, N, d, causal, -1, causal ? 0 : -1, nullptr, scale,
+                      dtype, stream, 1, 0, nullptr, nullptr, &dr);
 }
 
 extern "C" fa_status fa_fwd_f16(const void *q, const void *k, const void *v, void *o,

@@ -222,3 +222,43 @@ def test_split_unsupported_and_misaligned():
     assert scall(d=32) == fa.FA_ERR_UNSUPPORTED
     assert scall(ws=SWS + 4) == fa.FA_ERR_MISALIGNED
     assert scall(k=K + 2) == fa.FA_ERR_MISALIGNED
+
+
+# ---------------------------------------------------------------- dropout
+
+def dcall(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=64, d=128, causal=0, scale=0.125, p=0.1,
+          seed=(1 << 40) + 7, offset=3, dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, causal, scale, p, seed, offset, dtype,
+                             None)
+
+
+def dbcall(q=Q, k=K, v=V, o=O, do=DO, lse=L, ws=WS, dq=DQ, dk=DK, dv=DV, B=1, H=1, N=64,
+           d=128, causal=0, scale=0.125, p=0.1, seed=5, offset=0, dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_bwd_dropout(q, k, v, o, do, lse, ws, dq, dk, dv, B, H, N, d, causal, scale, p,
+                             seed, offset, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [dict(p=1.0), dict(p=-0.01), dict(p=math.nan), dict(p=2.0),
+                                dict(causal=2), dict(q=0), dict(lse=0), dict(B=0),
+                                dict(scale=math.nan), dict(dtype=9), dict(o=K + 64)])
+def test_dropout_fwd_invalid(kw):
+    assert dcall(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_dropout_fwd_unsupported_and_misaligned():
+    assert dcall(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert dcall(q=Q + 4) == fa.FA_ERR_MISALIGNED
+    assert dcall(lse=L + 2) == fa.FA_ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("kw", [dict(p=1.0), dict(p=-0.5), dict(p=math.inf), dict(p=math.nan),
+                                dict(causal=-1), dict(ws=0), dict(dv=0), dict(N=0),
+                                dict(dq=DK), dict(ws=Q)])
+def test_dropout_bwd_invalid(kw):
+    assert dbcall(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_dropout_bwd_unsupported_and_misaligned():
+    assert dbcall(d=256) == fa.FA_ERR_UNSUPPORTED
+    assert dbcall(dk=DK + 8) == fa.FA_ERR_MISALIGNED
+    assert dbcall(ws=WS + 4) == fa.FA_ERR_MISALIGNED
