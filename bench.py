@@ -9,14 +9,17 @@ to stderr.
   python bench.py [--gpus 1] [--steps 50] [--warmup 10]
                   [--workload n8k_causal_peaky] [--secondary n4k_causal]
                   [--backward n8k_causal_peaky] [--window n8k_causal_peaky:1023:0]
-                  [--split n4k_h4_causal:4] [--no-cpu-baseline] [--mode copy]
+                  [--split n4k_h4_causal:4] [--dropout n8k_causal_peaky:0.1]
+                  [--no-cpu-baseline] [--mode copy]
 
 The headline workload is B=1 H=32 N=8192 d=128 bf16 causal with Q,K x3;
 B=2 H=16 N=4096 d=128 bf16 causal is reported beside it, and the backward
 pass (fa_bwd) of the headline workload under "backward", and a sliding-window
 forward (fa_fwd_window, each query sees the 1024 keys ending at itself) under
-"window", and fa_fwd against fa_fwd_split on a few-head shape under "split".  FLOP =
-4*B*H*N^2*d, halved when causal (backward: 2.5 times that).
+"window", and fa_fwd against fa_fwd_split on a few-head shape under "split", and
+the dropout forward and backward (fa_fwd_dropout, fa_bwd_dropout, p = 0.1) of the
+headline workload under "dropout".  FLOP = 4*B*H*N^2*d, halved when causal
+(backward: 2.5 times that).
 """
 from __future__ import annotations
 
@@ -234,6 +237,59 @@ def time_split(w, num_splits: int, steps: int, warmup: int, seed: int = 0):
     return out
 
 
+def event_times(launch, stream, steps: int, warmup: int):
+    """Per-call times (ms, sorted) of `steps` calls of launch(), each
+    bracketed by HIP events on `stream`, after `warmup` untimed calls."""
+    import torch
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        launch()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ev)
+
+
+def time_dropout(w, p_drop: float, steps: int, warmup: int, seed: int = 0):
+    """fa_fwd_dropout, then fa_bwd_dropout on its o and lse, on the
+    workload's inputs: mean per-call times (ms) of each."""
+    import torch
+    import io_aware_transformer_amd as fa
+    from io_aware_transformer_amd.inputs import make_qkv, make_workload
+
+    dev = torch.device("cuda", 0)
+    q, k, v = (t.to(dev) for t in make_workload(w, seed=seed))
+    do = make_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=seed + 12345)[0].to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N) // 4, dtype=torch.float32,
+                     device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    stream = torch.cuda.current_stream(dev)
+    dt = fa.FA_DTYPE_F16 if w.dtype == "f16" else fa.FA_DTYPE_BF16
+    seed_rng, offset = 0x243F6A8885A308D3, 0
+
+    def fwd():
+        st = fa.fa_fwd_dropout(q, k, v, o, lse, w.B, w.H, w.N, w.d, int(w.causal), w.scale,
+                               p_drop, seed_rng, offset, dt, stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    def bwd():
+        st = fa.fa_bwd_dropout(q, k, v, o, do, lse, ws, dq, dk, dv, w.B, w.H, w.N, w.d,
+                               int(w.causal), w.scale, p_drop, seed_rng, offset, dt, stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    tf = event_times(fwd, stream, steps, warmup)
+    tb = event_times(bwd, stream, steps, warmup)
+    return {"fwd_ms": sum(tf) / len(tf), "bwd_ms": sum(tb) / len(tb)}
+
+
 def cpu_baseline(w, inputs, outputs, target_s: float):
     """The fp64 oracle on a bounded, evenly spaced sample of query rows of
     the same workload, timed on the host cores.  The same rows double as a
@@ -347,6 +403,9 @@ def main() -> int:
                          "('none' to skip)")
     ap.add_argument("--split", default="n4k_h4_causal:4",
                     help="WORKLOAD:SPLITS split-key forward reported beside ('none' to skip)")
+    ap.add_argument("--dropout", default="n8k_causal_peaky:0.1",
+                    help="WORKLOAD:P dropout forward and backward reported beside "
+                         "('none' to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench")
@@ -463,6 +522,21 @@ def main() -> int:
                          "ms_fa_fwd_split": round(rs["fa_fwd_split"], 5),
                          "tflops_fa_fwd": round(tp, 2), "tflops_fa_fwd_split": round(ts, 2),
                          "frac_fa_fwd_split": round(ts / PEAK_BF16_TFLOPS, 4)}
+
+    if args.dropout and args.dropout != "none":
+        dname, pd = args.dropout.split(":")
+        wd = WORKLOADS[dname]
+        rd = time_dropout(wd, float(pd), args.steps, args.warmup)
+        tf = wd.flops / (rd["fwd_ms"] * 1e-3) / 1e12
+        tbw = 2.5 * wd.flops / (rd["bwd_ms"] * 1e-3) / 1e12
+        log(f"bench: dropout p={pd} on {wd.name}: forward {rd['fwd_ms']*1e3:.1f} us "
+            f"({tf:.1f} TFLOP/s), backward {rd['bwd_ms']*1e3:.1f} us ({tbw:.1f} TFLOP/s)")
+        line["dropout"] = {"workload": wd.name, "p_drop": float(pd),
+                           "fwd_ms_mean": round(rd["fwd_ms"], 5),
+                           "fwd_tflops": round(tf, 2), "fwd_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                           "bwd_ms_mean": round(rd["bwd_ms"], 5),
+                           "bwd_tflops": round(tbw, 2),
+                           "bwd_frac": round(tbw / PEAK_BF16_TFLOPS, 4)}
 
     if not args.no_cpu_baseline:
         cb, par = cpu_baseline(w, res["inputs"], res["outputs"], args.cpu_seconds)
