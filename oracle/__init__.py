@@ -112,10 +112,15 @@ def _bind(lib):
                                             u64, u32, p, p]
     lib.oracle_attn_bwd_dropout.argtypes = [p, p, p, p, p, i32, i64, i64, i64, i64, i32, f64,
                                             i32, u64, u32, p, p, p]
+    lib.oracle_attn_fwd_dropout_rows.argtypes = [p, p, p, i32, i64, i64, i64, i64, i32, f64,
+                                                 i32, u64, u32, p, i64, p, p]
+    lib.oracle_attn_bwd_dropout_rows.argtypes = [p, p, p, p, p, i32, i64, i64, i64, i64, i32,
+                                                 f64, i32, u64, u32, p, i64, p, i64, p, p, p]
     for name in ("oracle_decode", "oracle_num_threads", "oracle_attn_fwd",
                  "oracle_attn_fwd_rows", "oracle_attn_probs", "oracle_attn_fwd_tiled",
                  "oracle_attn_bwd", "oracle_attn_bwd_rows", "oracle_attn_fwd_masked",
-                 "oracle_dropout_factors", "oracle_attn_fwd_dropout", "oracle_attn_bwd_dropout"):
+                 "oracle_dropout_factors", "oracle_attn_fwd_dropout", "oracle_attn_bwd_dropout",
+                 "oracle_attn_fwd_dropout_rows", "oracle_attn_bwd_dropout_rows"):
         getattr(lib, name).restype = ctypes.c_int
     lib.oracle_softmax_1d.restype = None
     lib.oracle_softmax_online_1d.restype = None
@@ -364,10 +369,50 @@ def _impl_attn_bwd_dropout(lib, q, k, v, do, o, dtype, causal: bool, scale: floa
     return dq, dk, dv
 
 
+def _impl_attn_fwd_dropout_rows(lib, q, k, v, dtype, causal: bool, scale: float, T: int,
+                                seed: int, offset: int, rows):
+    """attn_fwd_dropout on selected flat rows (b*H+h)*N+i.
+    Returns (o [n_rows,d], lse [n_rows])."""
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    B, H, N, d = _shape(q, k, v)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    o = np.empty((rows.size, d), dtype=np.float64)
+    lse = np.empty((rows.size,), dtype=np.float64)
+    _check(lib.oracle_attn_fwd_dropout_rows(_ptr(q), _ptr(k), _ptr(v), _dtype_code(dtype), B, H,
+                                            N, d, int(bool(causal)), float(scale), int(T),
+                                            int(seed), int(offset), _ptr(rows), rows.size,
+                                            _ptr(o), _ptr(lse)),
+           "oracle_attn_fwd_dropout_rows")
+    return o, lse
+
+
+def _impl_attn_bwd_dropout_rows(lib, q, k, v, do, o, dtype, causal: bool, scale: float, T: int,
+                                seed: int, offset: int, qrows, krows):
+    """attn_bwd_dropout (o given) on flat query rows qrows (dq) and flat key
+    rows krows (dk, dv).  Returns (dq [n_q,d], dk [n_k,d], dv [n_k,d])."""
+    q, k, v, do = _bits(q), _bits(k), _bits(v), _bits(do)
+    B, H, N, d = _shape(q, k, v)
+    o = _given_o(o, q.shape)
+    if o is None:
+        raise ValueError("the dropout backward takes the row term from a given o")
+    qrows = np.ascontiguousarray(qrows, dtype=np.int64)
+    krows = np.ascontiguousarray(krows, dtype=np.int64)
+    dq = np.empty((qrows.size, d), dtype=np.float64)
+    dk = np.empty((krows.size, d), dtype=np.float64)
+    dv = np.empty((krows.size, d), dtype=np.float64)
+    _check(lib.oracle_attn_bwd_dropout_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(o),
+                                            _dtype_code(dtype), B, H, N, d, int(bool(causal)),
+                                            float(scale), int(T), int(seed), int(offset),
+                                            _ptr(qrows), qrows.size, _ptr(krows), krows.size,
+                                            _ptr(dq), _ptr(dk), _ptr(dv)),
+           "oracle_attn_bwd_dropout_rows")
+    return dq, dk, dv
+
+
 _API = ("num_threads", "decode", "softmax_1d", "softmax_online_1d", "attn_fwd",
         "attn_fwd_rows", "attn_probs", "attn_fwd_tiled", "attn_bwd", "attn_bwd_rows",
         "attn_fwd_masked", "philox4x32_10", "dropout_factors", "attn_fwd_dropout",
-        "attn_bwd_dropout")
+        "attn_bwd_dropout", "attn_fwd_dropout_rows", "attn_bwd_dropout_rows")
 
 
 class Oracle:
@@ -411,3 +456,5 @@ philox4x32_10 = _module_fn("philox4x32_10")
 dropout_factors = _module_fn("dropout_factors")
 attn_fwd_dropout = _module_fn("attn_fwd_dropout")
 attn_bwd_dropout = _module_fn("attn_bwd_dropout")
+attn_fwd_dropout_rows = _module_fn("attn_fwd_dropout_rows")
+attn_bwd_dropout_rows = _module_fn("attn_bwd_dropout_rows")

@@ -785,6 +785,34 @@ int oracle_dropout_factors(int64_t BH, int64_t N, uint64_t seed, uint32_t offset
     return 0;
 }
 
+/* Flat row r = (b*H+h)*N + i with dropout: o_i = sum_j P_ij Z_ij v_j into
+ * orow, lse as without dropout into *lse; s is scratch for N scores. */
+static void dropout_fwd_row(const problem *p, int64_t r, double *s, int T, uint64_t seed,
+                            uint32_t offset, double *orow, double *lse)
+{
+    const int64_t N = p->N, d = p->d;
+    const int64_t bh = r / N, i = r % N;
+    const double *qi = p->q + r * d;
+    const double *kh = p->k + bh * N * d, *vh = p->v + bh * N * d;
+    const int64_t nkeys = p->causal ? i + 1 : N;
+    double m = -INFINITY;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
+        s[j] = p->scale * dot;
+        if (s[j] > m) m = s[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < nkeys; ++j) l += exp(s[j] - m);
+    for (int64_t c = 0; c < d; ++c) orow[c] = 0.0;
+    for (int64_t j = 0; j < nkeys; ++j) {
+        const double w = exp(s[j] - m) / l * dropout_factor(bh, i, j, seed, offset, T);
+        if (w == 0.0) continue;
+        for (int64_t c = 0; c < d; ++c) orow[c] += w * vh[j * d + c];
+    }
+    *lse = m + log(l);
+}
+
 /* Forward with dropout: o_i = sum_j P_ij Z_ij v_j, lse as without dropout. */
 int oracle_attn_fwd_dropout(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                             int dtype, int64_t B, int64_t H, int64_t N, int64_t d,
@@ -805,29 +833,39 @@ int oracle_attn_fwd_dropout(const uint16_t *q, const uint16_t *k, const uint16_t
             fail = 1;
         } else {
 #pragma omp for schedule(dynamic, 16)
-            for (int64_t r = 0; r < rows; ++r) {
-                const int64_t bh = r / N, i = r % N;
-                const double *qi = p.q + r * d;
-                const double *kh = p.k + bh * N * d, *vh = p.v + bh * N * d;
-                const int64_t nkeys = causal ? i + 1 : N;
-                double m = -INFINITY;
-                for (int64_t j = 0; j < nkeys; ++j) {
-                    double dot = 0.0;
-                    for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
-                    s[j] = scale * dot;
-                    if (s[j] > m) m = s[j];
-                }
-                double l = 0.0;
-                for (int64_t j = 0; j < nkeys; ++j) l += exp(s[j] - m);
-                double *orow = o + r * d;
-                for (int64_t c = 0; c < d; ++c) orow[c] = 0.0;
-                for (int64_t j = 0; j < nkeys; ++j) {
-                    const double w = exp(s[j] - m) / l * dropout_factor(bh, i, j, seed, offset, T);
-                    if (w == 0.0) continue;
-                    for (int64_t c = 0; c < d; ++c) orow[c] += w * vh[j * d + c];
-                }
-                lse[r] = m + log(l);
-            }
+            for (int64_t r = 0; r < rows; ++r)
+                dropout_fwd_row(&p, r, s, T, seed, offset, o + r * d, lse + r);
+        }
+        free(s);
+    }
+    free_problem(&p);
+    return fail ? -2 : 0;
+}
+
+/* The same on the flat rows rows[] only: o_rows [n_rows, d], lse_rows. */
+int oracle_attn_fwd_dropout_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                 int dtype, int64_t B, int64_t H, int64_t N, int64_t d,
+                                 int causal, double scale, int T, uint64_t seed,
+                                 uint32_t offset, const int64_t *rows, int64_t n_rows,
+                                 double *o_rows, double *lse_rows)
+{
+    if (T < 0 || T > 256) return -1;
+    for (int64_t t = 0; t < n_rows; ++t)
+        if (rows[t] < 0 || rows[t] >= B * H * N) return -1;
+    problem p;
+    int rc = load_problem(&p, q, k, v, dtype, B, H, N, d, causal, scale);
+    if (rc) return rc;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t t = 0; t < n_rows; ++t)
+                dropout_fwd_row(&p, rows[t], s, T, seed, offset, o_rows + t * d, lse_rows + t);
         }
         free(s);
     }
@@ -885,6 +923,95 @@ int oracle_attn_bwd_dropout(const uint16_t *q, const uint16_t *k, const uint16_t
         free(prow);
         free(dprow);
     }
+    free_bproblem(&bp);
+    return fail ? -2 : 0;
+}
+
+/* Sampled dropout gradients (o given, as oracle_attn_bwd_dropout): dq for
+ * the flat query rows qrows[], dk and dv for the flat key rows krows[],
+ * packed [n_q,d] and [n_k,d].  As in oracle_attn_bwd_rows, the heads of the
+ * sampled keys are evaluated row by row first (lse_i and D_i kept). */
+int oracle_attn_bwd_dropout_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                 const uint16_t *dO, const uint16_t *o, int dtype, int64_t B,
+                                 int64_t H, int64_t N, int64_t d, int causal, double scale,
+                                 int T, uint64_t seed, uint32_t offset, const int64_t *qrows,
+                                 int64_t n_q, const int64_t *krows, int64_t n_k,
+                                 double *dq_rows, double *dk_rows, double *dv_rows)
+{
+    if (T < 0 || T > 256 || !o) return -1;
+    const int64_t total = B * H * N;
+    for (int64_t t = 0; t < n_q; ++t)
+        if (qrows[t] < 0 || qrows[t] >= total) return -1;
+    for (int64_t t = 0; t < n_k; ++t)
+        if (krows[t] < 0 || krows[t] >= total) return -1;
+    bproblem bp;
+    int rc = load_bproblem(&bp, q, k, v, dO, o, dtype, B, H, N, d, causal, scale);
+    if (rc) return rc;
+    int fail = 0;
+    char *need = (char *)calloc((size_t)(B * H > 0 ? B * H : 1), 1);
+    double *Dall = (double *)malloc((size_t)(total > 0 ? total : 1) * sizeof(double));
+    double *Lall = (double *)malloc((size_t)(total > 0 ? total : 1) * sizeof(double));
+    if (!need || !Dall || !Lall) {
+        free(need); free(Dall); free(Lall); free_bproblem(&bp);
+        return -2;
+    }
+    for (int64_t t = 0; t < n_k; ++t) need[krows[t] / N] = 1;
+#pragma omp parallel
+    {
+        double *prow = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        double *dprow = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (!prow || !dprow) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < total; ++r)
+                if (need[r / N]) Dall[r] = grad_row(&bp, r / N, r % N, prow, dprow, Lall + r);
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t t = 0; t < n_q; ++t) {
+                const int64_t bh = qrows[t] / N, i = qrows[t] % N;
+                const double D = grad_row(&bp, bh, i, prow, dprow, NULL);
+                const int64_t nkeys = causal ? i + 1 : N;
+                const double *kh = bp.p.k + bh * N * d;
+                double *out = dq_rows + t * d;
+                for (int64_t c = 0; c < d; ++c) out[c] = 0.0;
+                for (int64_t j = 0; j < nkeys; ++j) {
+                    const double z = dropout_factor(bh, i, j, seed, offset, T);
+                    const double ds = prow[j] * (z * dprow[j] - D);
+                    for (int64_t c = 0; c < d; ++c) out[c] += scale * ds * kh[j * d + c];
+                }
+            }
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t t = 0; t < n_k; ++t) {
+                const int64_t bh = krows[t] / N, j = krows[t] % N;
+                double *ok = dk_rows + t * d, *ov = dv_rows + t * d;
+                for (int64_t c = 0; c < d; ++c) ok[c] = ov[c] = 0.0;
+                const double *kj = bp.p.k + (bh * N + j) * d;
+                const double *vj = bp.p.v + (bh * N + j) * d;
+                for (int64_t i = causal ? j : 0; i < N; ++i) {
+                    const double *qi = bp.p.q + (bh * N + i) * d;
+                    const double *doi = bp.dO + (bh * N + i) * d;
+                    double dot = 0.0, dp = 0.0;
+                    for (int64_t c = 0; c < d; ++c) {
+                        dot += qi[c] * kj[c];
+                        dp += doi[c] * vj[c];
+                    }
+                    const double pij = exp(scale * dot - Lall[bh * N + i]);
+                    const double z = dropout_factor(bh, i, j, seed, offset, T);
+                    const double ds = pij * (z * dp - Dall[bh * N + i]);
+                    for (int64_t c = 0; c < d; ++c) {
+                        ok[c] += scale * ds * qi[c];
+                        ov[c] += pij * z * doi[c];
+                    }
+                }
+            }
+        }
+        free(prow);
+        free(dprow);
+    }
+    free(need);
+    free(Dall);
+    free(Lall);
     free_bproblem(&bp);
     return fail ? -2 : 0;
 }

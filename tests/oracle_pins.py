@@ -418,6 +418,32 @@ def pin_dropout(orc) -> bool:
     return ok
 
 
+def pin_dropout_rows(orc) -> bool:
+    """The sampled-row dropout functions against the full ones."""
+    import oracle as _o
+    seed, off = 0xFEEDFACE12345678, 3
+    T = _o.dropout_threshold(0.25)
+    q, k, v = _qkv(2, 2, 45, 8, "f16", seed=31)
+    do = _qkv(2, 2, 45, 8, "f16", seed=32)[0]
+    qr = np.array([0, 7, 44, 45, 90, 179], dtype=np.int64)
+    kr = np.array([0, 1, 44, 46, 100, 179], dtype=np.int64)
+    ok = True
+    for causal in (False, True):
+        o, lse = orc.attn_fwd_dropout(bits(q), bits(k), bits(v), "f16", causal, 0.35, T, seed, off)
+        a, b = orc.attn_fwd_dropout_rows(bits(q), bits(k), bits(v), "f16", causal, 0.35, T, seed,
+                                         off, qr)
+        ok &= bool(np.array_equal(a, o.reshape(-1, 8)[qr]) and np.array_equal(b, lse.reshape(-1)[qr]))
+        o16 = to_tensor(o, "f16")
+        dq, dk, dv = orc.attn_bwd_dropout(bits(q), bits(k), bits(v), bits(do), bits(o16), "f16",
+                                          causal, 0.35, T, seed, off)
+        a, b, c = orc.attn_bwd_dropout_rows(bits(q), bits(k), bits(v), bits(do), bits(o16), "f16",
+                                            causal, 0.35, T, seed, off, qr, kr)
+        ok &= _close(a, dq.reshape(-1, 8)[qr], 1e-12)
+        ok &= _close(b, dk.reshape(-1, 8)[kr], 1e-12)
+        ok &= _close(c, dv.reshape(-1, 8)[kr], 1e-12)
+    return ok
+
+
 PINS = {
     "brute_force": pin_brute_force,
     "python_loops": pin_python_loops,
@@ -436,6 +462,7 @@ PINS = {
     "masked": pin_masked,
     "philox_kat": pin_philox_kat,
     "dropout": pin_dropout,
+    "dropout_rows": pin_dropout_rows,
 }
 
 

@@ -284,8 +284,21 @@ def test_tiny_workload_against_library(oracle_mod):
 
 # Each entry plants one plausible mistake in a copy of oracle.c; the pins
 # above must catch every one.  (old text, new text, what the mistake is)
+# the key-row loop of oracle_attn_bwd_rows up to its dS (the dropout
+# variant differs there), making the loop's mutation site unique
+_ROWS_LOOP = ("\n                    const double *qi = bp.p.q + (bh * N + i) * d;"
+              "\n                    const double *doi = bp.dO + (bh * N + i) * d;"
+              "\n                    double dot = 0.0, dp = 0.0;"
+              "\n                    for (int64_t c = 0; c < d; ++c) {"
+              "\n                        dot += qi[c] * kj[c];"
+              "\n                        dp += doi[c] * vj[c];"
+              "\n                    }"
+              "\n                    const double pij = exp(scale * dot - Lall[bh * N + i]);"
+              "\n                    const double ds = pij * (dp")
+
 MUTANTS = [
-    ("s[j] = p->scale * dot;", "s[j] = dot;", "dropped scale"),
+    ("s[j] = p->scale * dot;\n        if (s[j] > m) m = s[j];\n    }\n    /* pass 2",
+     "s[j] = dot;\n        if (s[j] > m) m = s[j];\n    }\n    /* pass 2", "dropped scale"),
     ("        double w = exp(s[j] - m);", "        double w = exp(m - s[j]);", "sign of the exponent"),
     ("const double w = exp(s[j] - m);", "const double w = exp(m - s[j]);",
      "mask: sign of the exponent"),
@@ -296,7 +309,8 @@ MUTANTS = [
     ("if (lse_out) *lse_out = m + log(l);", "if (lse_out) *lse_out = log(l);",
      "bwd rows: row lse without the max"),
     ("o_out[c] += w * vh[j * d + c];", "o_out[c] += w * vh[i * d + c];", "V row index"),
-    ("dot += qi[c] * kh[j * d + c];\n        s[j]", "dot += qi[c] * kh[j * d + (d - 1 - c)];\n        s[j]",
+    ("dot += qi[c] * kh[j * d + c];\n        s[j] = p->scale * dot;\n        if (s[j] > m) m = s[j];\n    }\n    /* pass 2",
+     "dot += qi[c] * kh[j * d + (d - 1 - c)];\n        s[j] = p->scale * dot;\n        if (s[j] > m) m = s[j];\n    }\n    /* pass 2",
      "feature index of K reversed"),
     ("dot += qi[c] * kh[j * d + c];\n        prow[j]",
      "dot += qi[c] * kh[j * d + (d - 1 - c)];\n        prow[j]",
@@ -334,17 +348,20 @@ MUTANTS = [
     ("dvh[j * d + c] += prow[j] * doh[i * d + c];", "dvh[j * d + c] += prow[j] * doh[j * d + c];",
      "bwd: dV row index"),
     ("D += prow[j] * dp;", "D += dp;", "bwd: row term without P"),
-    ("const int64_t nkeys = p->causal ? i + 1 : N;\n    double m = -INFINITY;",
-     "const int64_t nkeys = p->causal ? N : N;\n    double m = -INFINITY;",
+    ("const int64_t nkeys = p->causal ? i + 1 : N;\n    double m = -INFINITY;\n    for (int64_t j = 0; j < nkeys; ++j) {\n        double dot = 0.0;\n        for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];\n        prow[j]",
+     "const int64_t nkeys = p->causal ? N : N;\n    double m = -INFINITY;\n    for (int64_t j = 0; j < nkeys; ++j) {\n        double dot = 0.0;\n        for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];\n        prow[j]",
      "bwd: causal mask dropped in the row weights"),
     ("dp += doi[c] * vh[j * d + c];", "dp += doi[c] * vh[i * d + c];", "bwd: dP row index of V"),
     ("const double ds = pij * (dp - Dall[bh * N + i]);",
      "const double ds = pij * (Dall[bh * N + i] - dp);", "bwd rows: sign of dS"),
-    ("for (int64_t i = causal ? j : 0; i < N; ++i) {",
-     "for (int64_t i = causal ? j + 1 : 0; i < N; ++i) {", "bwd rows: causal diagonal dropped"),
-    ("const double pij = exp(scale * dot - Lall[bh * N + i]);",
-     "const double pij = exp(scale * dot);", "bwd rows: P without lse"),
-    ("out[c] += scale * ds * kh[j * d + c];", "out[c] += ds * kh[j * d + c];",
+    ("for (int64_t i = causal ? j : 0; i < N; ++i) {" + _ROWS_LOOP,
+     "for (int64_t i = causal ? j + 1 : 0; i < N; ++i) {" + _ROWS_LOOP,
+     "bwd rows: causal diagonal dropped"),
+    ("const double pij = exp(scale * dot - Lall[bh * N + i]);\n                    const double ds",
+     "const double pij = exp(scale * dot);\n                    const double ds",
+     "bwd rows: P without lse"),
+    ("(dprow[j] - D);\n                    for (int64_t c = 0; c < d; ++c) out[c] += scale * ds",
+     "(dprow[j] - D);\n                    for (int64_t c = 0; c < d; ++c) out[c] += ds",
      "bwd rows: dQ without scale"),
     ("for (int64_t c = 0; c < d; ++c) D += doi[c] * oi[c];",
      "for (int64_t c = 0; c < d; ++c) D += doi[c] * oi[0];", "bwd: given-o row term index"),
@@ -365,8 +382,19 @@ MUTANTS = [
      "dropout: byte index transposed"),
     ("< (unsigned)T ? 256.0 / T : 0.0;", "<= (unsigned)T ? 256.0 / T : 0.0;",
      "dropout: keep threshold off by one"),
-    ("const double ds = prow[j] * (z * dprow[j] - D);", "const double ds = prow[j] * (dprow[j] - D);",
+    ("const double ds = prow[j] * (z * dprow[j] - D);\n                        for",
+     "const double ds = prow[j] * (dprow[j] - D);\n                        for",
      "dropout bwd: dS without the keep factor"),
+    ("const double ds = prow[j] * (z * dprow[j] - D);\n                    for",
+     "const double ds = prow[j] * (dprow[j] - D);\n                    for",
+     "dropout bwd rows: dQ without the keep factor"),
+    ("const double ds = pij * (z * dp - Dall[bh * N + i]);",
+     "const double ds = pij * (dp - Dall[bh * N + i]);", "dropout bwd rows: dK without the keep factor"),
+    ("ov[c] += pij * z * doi[c];", "ov[c] += pij * doi[c];",
+     "dropout bwd rows: dV without the keep factor"),
+    ("dropout_fwd_row(&p, rows[t], s, T, seed, offset, o_rows + t * d, lse_rows + t);",
+     "dropout_fwd_row(&p, rows[t], s, T, seed, offset + 1, o_rows + t * d, lse_rows + t);",
+     "dropout fwd rows: wrong offset"),
     ("dvh[j * d + c] += prow[j] * z * doh[i * d + c];", "dvh[j * d + c] += prow[j] * doh[i * d + c];",
      "dropout bwd: dV without the keep factor"),
 ]
@@ -441,7 +469,7 @@ def test_masked_rejects_bad_lengths(oracle_mod):
 
 # ---------------------------------------------------------------- dropout
 
-@pytest.mark.parametrize("name", ["philox_kat", "dropout"])
+@pytest.mark.parametrize("name", ["philox_kat", "dropout", "dropout_rows"])
 def test_dropout_pins(oracle_mod, name):
     assert PINS[name](oracle_mod)
 
