@@ -284,3 +284,81 @@ def test_end_to_end_same_pattern(dtype, causal):
     fdk = scale * (np.swapaxes(P, -1, -2) @ (b[..., None] * np.abs(q.double().numpy())))
     rep = compare_grads(got, ref, dtype, floor=(fdq, fdk, np.zeros_like(fdq)))
     assert rep["ok"], rep
+
+
+# ---------------------------------------------------------------- full size
+
+# The dropout launch bench.py times: the B1 H32 N8192 d128 bf16 causal
+# workload with Q, K x3, p = 0.1, this seed and offset 0.
+BENCH_DROPOUT = ("n8k_causal_peaky", 0.1, 0x243F6A8885A308D3, 0)
+
+
+def _sample_rows(BH, N, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([rng.integers(0, BH * N, n),
+                                     [0, 1, N - 1, N, BH * N - 2, BH * N - 1]]))
+
+
+def test_fwd_full_size_sampled():
+    """fa_fwd_dropout on the whole benchmarked workload; sampled rows against
+    the oracle's row variant.  The P-operand floor uses Z <= 256/T:
+    pf <= u (256/T) sum_j P_ij |v_jc|, P from the row's fp64 softmax."""
+    from io_aware_transformer_amd.inputs import WORKLOADS, make_workload
+    name, p, seed, off = BENCH_DROPOUT
+    w = WORKLOADS[name]
+    note(f"[dropout fwd] full size {name}: {w.note}, p={p}")
+    q, k, v = make_workload(w, seed=0)
+    o, lse = gpu_fwd_dropout(q, k, v, w.causal, w.scale, p, seed, off)
+    rows = _sample_rows(w.B * w.H, w.N, 300, 11)
+    ro, rl = oracle.attn_fwd_dropout_rows(bits(q), bits(k), bits(v), w.dtype, w.causal,
+                                          w.scale, thr(p), seed, off, rows)
+    og = o.reshape(-1, w.d)[torch.from_numpy(rows)].double().numpy()
+    lg = lse.reshape(-1)[torch.from_numpy(rows)].double().numpy()
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    assert float(np.abs(lg - rl).max()) <= TOL_LSE
+    err = np.abs(og - ro)
+    tol = TOL_O[w.dtype]
+    if err.max() > tol:
+        q64 = q.double().numpy().reshape(-1, w.N, w.d)
+        k64 = k.double().numpy().reshape(-1, w.N, w.d)
+        v64 = np.abs(v.double().numpy().reshape(-1, w.N, w.d))
+        pf = np.empty_like(ro)
+        for t, r in enumerate(rows):
+            h, i = divmod(int(r), w.N)
+            s = w.scale * (k64[h] @ q64[h, i])
+            if w.causal:
+                s[i + 1:] = -np.inf
+            pr = np.exp(s - s.max())
+            pf[t] = (pr / pr.sum()) @ v64[h]
+        pf *= _U[w.dtype] * 256.0 / thr(p)
+        bad = err > tol + pf + 0.5 * ulp16(np.abs(ro) + pf, w.dtype)
+        assert not bad.any(), (float(err.max()), int(bad.sum()))
+
+
+def test_bwd_full_size_sampled():
+    """fa_bwd_dropout on the whole benchmarked workload, handed the oracle's
+    full dropout forward (o rounded to bf16, lse in fp32); sampled query rows
+    (dq) and key rows of four heads (dk, dv) against the oracle's row
+    variant, R16's normalised tolerance."""
+    from io_aware_transformer_amd.inputs import WORKLOADS, make_workload
+    name, p, seed, off = BENCH_DROPOUT
+    w = WORKLOADS[name]
+    note(f"[dropout bwd] full size {name}: {w.note}, p={p}")
+    q, k, v = make_workload(w, seed=0)
+    do = make_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=12345)[0]
+    o, lse = oracle_given(q, k, v, w.causal, w.scale, p, seed, off)
+    got = gpu_bwd_dropout(q, k, v, o, lse, do, w.causal, w.scale, p, seed, off)
+    BH, N = w.B * w.H, w.N
+    rng = np.random.default_rng(5)
+    qrows = _sample_rows(BH, N, 48, 6)
+    heads = rng.choice(BH, size=min(4, BH), replace=False)
+    krows = np.unique(np.concatenate([h * N + rng.integers(0, N, 12) for h in heads] +
+                                     [[heads[0] * N, heads[0] * N + N - 1]]))
+    ref = oracle.attn_bwd_dropout_rows(bits(q), bits(k), bits(v), bits(do), bits(o), w.dtype,
+                                       w.causal, w.scale, thr(p), seed, off, qrows, krows)
+    gq = got[0].reshape(-1, w.d)[torch.from_numpy(qrows)]
+    gk = got[1].reshape(-1, w.d)[torch.from_numpy(krows)]
+    gv = got[2].reshape(-1, w.d)[torch.from_numpy(krows)]
+    rep = compare_grads((gq, gk, gv), ref, w.dtype)
+    print(name, rep)
+    assert rep["ok"], rep
