@@ -35,6 +35,11 @@
 // need no mask: their Q, K, V and dO read as zero from the buffer range
 // check, so every term they add to a stored output is zero.
 //
+// Dropout (fa_bwd_dropout): the walking kernels take a DROP flag that
+// redraws the forward pass's keep factors Z from the same Philox counters
+// ([P-wmrh] §4.2: forward and backward must draw one pattern) and computes
+// dV = (P o Z)^T dO and dS = P o (Z o dP - D).
+//
 // Tiles in LDS use one 16-byte-chunk XOR swizzle that is bank-conflict free
 // both for ds_read_b128 of 16 rows at one logical chunk and for the 4-row x
 // 64-byte footprint of ds_read_b64_tr_b16, since Q, dO (dK/dV kernel) and K

@@ -57,6 +57,14 @@
 //
 // Causal K/V tiles wholly above the diagonal are never visited ([P-baidu]
 // §7); the last Q block of a ragged N masks keys >= N and stores no rows >= N.
+//
+// One kernel template serves every forward entry point: MODE 0 / 1 (all
+// keys / causal: fa_fwd), 2 (sliding window and valid lengths, the mask
+// kinds of [P-baidu] §8: fa_fwd_window), 3 (one key segment per grid row,
+// merged by fa_fwd_merge_kernel: fa_fwd_split), and the DROP flag on modes
+// 0 / 1 (dropout fused into the kernel, [P-wmrh] §1.2: fa_fwd_dropout).
+// Each variant is a compile-time instantiation, so the tuned full and causal
+// kernels carry none of the others' code.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
