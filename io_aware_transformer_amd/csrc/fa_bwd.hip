@@ -244,9 +244,9 @@ void fa_bwd_delta_kernel(const u16 *__restrict__ O, const u16 *__restrict__ dO,
 // DROP: the dropout of the forward pass, redrawn.  dV^T += dO^T (P o Z) and
 // dS = P o (Z o dP - D).  A lane here holds one key and 16 queries, while a
 // Philox call yields 16 keys of one query, so each lane makes the call of
-// (query qs + l32, key half hh) of the step and the 32 x 32 bytes are
-// transposed through a per-wave 1 KB LDS block: a byte transpose inside each
-// lane quad, 4 dword writes, one 16-byte read per lane.
+// (query qs + l32, key half hh) of each step and the 32 x 32 bytes are
+// transposed through a per-wave LDS block: a byte transpose inside each
+// lane quad, 4 dword writes, and in the step one 16-byte read per lane.
 template <int DT, int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
@@ -270,8 +270,9 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     __shared__ __attribute__((aligned(1024))) unsigned char o1s[QTB];
     __shared__ __attribute__((aligned(256))) float w0s[2 * kQT];
     __shared__ __attribute__((aligned(256))) float w1s[2 * kQT];
-    // dropout bytes of one step, per wave: [key 32][query half 2][g 4] words
-    __shared__ __attribute__((aligned(1024))) unsigned zs[DROP ? kWaves * 256 : 1];
+    // dropout bytes of one query tile, per wave: [step 2][key 32][query
+    // half 2][g 4] words
+    __shared__ __attribute__((aligned(1024))) unsigned zs[DROP ? kWaves * 512 : 1];
     auto qbuf = [&](auto b) -> LDS unsigned char * {
         if constexpr (decltype(b)::value == 0) return (LDS unsigned char *)q0s;
         else return (LDS unsigned char *)q1s;
@@ -388,27 +389,36 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     // quad transpose, word gk of lane (quad a = m/4, position e = m%4) holds,
     // for key 8gk + 4hh + e, the four queries 4a..4a+3: word a/2 of query
     // half a%2.
-    LDS unsigned *zw = (LDS unsigned *)zs + (DROP ? 256 * w : 0);
-    const QuadTranspose qtr(lane);
-    auto drop_bytes = [&](int qs) -> u32x4 {
-        const u32x4 r = philox4x32_10((unsigned)(qs + l32), (unsigned)(2 * (kw / 32) + hh),
-                                      (unsigned)bh, dr.offset, dr.seed_lo, dr.seed_hi);
+    // The bytes of a whole query tile are drawn before its steps, while only
+    // the K fragments and the accumulators are live, so no Philox state
+    // shares the registers with S and dP; a step reads its 16 bytes back
+    // with one ds_read_b128.
+    LDS unsigned *zw = (LDS unsigned *)zs + (DROP ? 512 * w : 0);
+    auto drop_tile = [&](int t) {
+        const QuadTranspose qtr(lane);
         const int a = l32 >> 2, e = l32 & 3;
-        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
 #pragma unroll
-        for (int gk = 0; gk < 4; ++gk)
-            zw[(8 * gk + 4 * hh + e) * 8 + (a & 1) * 4 + (a >> 1)] = qtr(r[gk]);
-        __builtin_amdgcn_wave_barrier();
-        const u32x4 z = *(const LDS u32x4 *)(zw + l32 * 8 + hh * 4);
-        __builtin_amdgcn_wave_barrier();
-        return z;
+        for (int u = 0; u < kQT / 32; ++u) {
+            const int qs = t * kQT + 32 * u;
+            if ((CAUSAL && qs + 31 < kw) || qs >= N) continue;   // step not computed
+            const u32x4 r = philox4x32_10((unsigned)(qs + l32), (unsigned)(2 * (kw / 32) + hh),
+                                          (unsigned)bh, dr.offset, dr.seed_lo, dr.seed_hi);
+#pragma unroll
+            for (int gk = 0; gk < 4; ++gk)
+                zw[256 * u + (8 * gk + 4 * hh + e) * 8 + (a & 1) * 4 + (a >> 1)] = qtr(r[gk]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    };
+    auto drop_bytes = [&](int u) -> u32x4 {
+        return *(const LDS u32x4 *)(zw + 256 * u + l32 * 8 + hh * 4);
     };
 
     // one step: 32 queries (sub-step u of the tile in buffers par).  Every
     // MFMA loop reads its LDS operands a fixed distance ahead, and the
     // interleave is pinned (scheduling-group barriers) so that neither the
     // reads crowd the registers nor each MFMA waits on its own read.
-    auto step = [&](auto par, int u, bool diag, int qs) {
+    auto step = [&](auto par, int u, bool diag) {
         LDS unsigned char *qb = qbuf(par);
         LDS unsigned char *ob = obuf(par);
         LDS float *wb = wbuf(par) + u * 2 * kWsRows;
@@ -474,7 +484,7 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         }
         // P = 2^(S c2 - lse log2 e), dS = P dP'; rows m = 8(r/4) + 4hh + r%4
         u32x4 zb;
-        if constexpr (DROP) zb = drop_bytes(qs);
+        if constexpr (DROP) zb = drop_bytes(u);
         u32x4 pp[2], dsp[2];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -535,10 +545,15 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     auto tile = [&](auto par, int t) {
         constexpr int P = decltype(par)::value;
         if (t + 1 < n_qt) issue(Buf<1 - P>{}, t + 1);
+        if constexpr (DROP) drop_tile(t);
 #pragma unroll
         for (int u = 0; u < kQT / 32; ++u) {
             const int qs = t * kQT + 32 * u;   // first query of the step
-            if (!CAUSAL || qs + 31 >= kw) step(par, u, CAUSAL && qs == kw, qs);
+            // under dropout a step wholly past N (which adds nothing) is
+            // skipped too: the branch keeps the register allocator from
+            // spilling across the fused steps of the non-causal kernel
+            if ((!CAUSAL || qs + 31 >= kw) && (!DROP || qs < N))
+                step(par, u, CAUSAL && qs == kw);
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_waitcnt(0);
