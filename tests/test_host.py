@@ -1,0 +1,92 @@
+"""CPU tests of the host-side pieces: the seeded input generator (the one
+module both the HIP path and the oracle read), the workload definitions the
+bench reports, and bench.py's command-line contract."""
+from __future__ import annotations
+
+import json
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from io_aware_transformer_amd.inputs import WORKLOADS, bits, make_qkv, make_workload
+from tests.conftest import ROOT
+
+
+def test_generator_is_deterministic_and_seed_dependent():
+    a = make_qkv(1, 2, 33, 64, "bf16", seed=5)
+    b = make_qkv(1, 2, 33, 64, "bf16", seed=5)
+    c = make_qkv(1, 2, 33, 64, "bf16", seed=6)
+    for x, y in zip(a, b):
+        assert np.array_equal(bits(x), bits(y))
+    assert not np.array_equal(bits(a[0]), bits(c[0]))
+    # q, k and v are distinct draws of one stream
+    assert not np.array_equal(bits(a[0]), bits(a[1]))
+
+
+@pytest.mark.parametrize("dtype,tdt", [("f16", torch.float16), ("bf16", torch.bfloat16)])
+def test_generator_follows_the_recipe(dtype, tdt):
+    """q, k, v = one CPU generator's randn draws in that order, q and k times
+    the gain in fp32, each cast once (round to nearest even)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(11)
+    shape = (2, 1, 17, 8)
+    q, k, v = (torch.randn(shape, generator=g, dtype=torch.float32) for _ in range(3))
+    got = make_qkv(*shape, dtype, seed=11, qk_gain=3.0)
+    want = ((q * 3.0).to(tdt), (k * 3.0).to(tdt), v.to(tdt))
+    for x, y in zip(got, want):
+        assert x.dtype == tdt and x.shape == shape
+        assert np.array_equal(bits(x), bits(y))
+
+
+def test_bits_rejects_other_types():
+    with pytest.raises(TypeError):
+        bits(torch.zeros(3))
+    with pytest.raises(ValueError):
+        make_qkv(1, 1, 2, 8, "f32")
+
+
+def test_workload_flops_convention():
+    for w in WORKLOADS.values():
+        full = 4.0 * w.B * w.H * w.N ** 2 * w.d
+        assert w.flops == (full / 2 if w.causal else full)
+        assert w.scale == float(np.float32(1.0 / np.sqrt(w.d)))
+    w = WORKLOADS["n8k_causal_peaky"]
+    assert (w.B, w.H, w.N, w.d, w.dtype, w.causal, w.qk_gain) == (1, 32, 8192, 128, "bf16",
+                                                                 True, 3.0)
+    q, k, v = make_workload(WORKLOADS["tiny"])
+    assert q.shape == (1, 2, 256, 64) and q.dtype == torch.float16
+
+
+def _bench(*args):
+    return subprocess.run([sys.executable, str(ROOT / "bench.py"), *args], capture_output=True,
+                          text=True, timeout=120)
+
+
+@pytest.mark.parametrize("n", ["2", "8"])
+def test_bench_refuses_more_than_one_gpu(n):
+    r = _bench("--gpus", n)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_bench_help_names_every_option():
+    r = _bench("--help")
+    assert r.returncode == 0
+    for opt in ("--gpus", "--steps", "--warmup", "--workload", "--backward", "--window",
+                "--split", "--dropout", "--no-cold", "--no-cpu-baseline"):
+        assert opt in r.stdout, opt
+
+
+def test_bench_without_gpu_fails_loudly():
+    """No GPU visible: a non-zero exit and no JSON line (never a CPU number)."""
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    r = _bench("--steps", "1", "--warmup", "0")
+    assert r.returncode != 0
+    for line in r.stdout.splitlines():
+        with pytest.raises(json.JSONDecodeError):
+            json.loads(line)
