@@ -707,14 +707,35 @@ void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     auto step = [&](auto par, int u, bool diag, int ks0) {
         LDS unsigned char *kb = kbuf(par);
         LDS unsigned char *vb = vbuf(par);
-        f32x16 s = {};
-#pragma unroll
-        for (int kk = 0; kk < KT; ++kk) s = E::mfma(rfrag(kb, u, kk), qf[kk], s);
-        f32x16 dp;
+        // S^T and dP'^T as two interleaved MFMA chains; operand i (K for even
+        // i, V for odd) read from LDS AH MFMAs ahead, the interleave pinned
+        f32x16 s = {}, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) dp[r] = DROP ? 0.f : -dd;
+        {
+            constexpr int NR = 2 * KT;
+            constexpr int AH = 3;
+            u16x8 a[NR];
+            auto frag = [&](int i) -> u16x8 {
+                return (i & 1) ? rfrag(vb, u, i >> 1) : rfrag(kb, u, i >> 1);
+            };
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kk = 0; kk < KT; ++kk) dp = E::mfma(rfrag(vb, u, kk), of[kk], dp);
+            for (int i = 0; i < AH; ++i) a[i] = frag(i);
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                if (i + AH < NR) a[i + AH] = frag(i + AH);
+                if (i & 1) dp = E::mfma(a[i], of[i >> 1], dp);
+                else s = E::mfma(a[i], qf[i >> 1], s);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i < NR - AH) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         // rows = keys ks0 + 8(r/4) + 4hh + r%4, column = query qrow; under
         // dropout register 4g + e is byte 4g + e of the step's call
         u32x4 zb;
@@ -739,11 +760,27 @@ void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             dsp[g >> 1][2 * (g & 1)] = E::pack2(ds[0], ds[1]);
             dsp[g >> 1][2 * (g & 1) + 1] = E::pack2(ds[2], ds[3]);
         }
+        // dQ^T += K^T dS^T, transposing reads of K two per MFMA, AH ahead
+        {
+            constexpr int NM = 2 * DB;
+            constexpr int AH = 2;
+            u16x8 tk[NM];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+            for (int i = 0; i < AH; ++i) tk[i] = tfrag(kb, u, i % DB, i / DB);
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-                dqa[db] = E::mfma(tfrag(kb, u, db, ks), __builtin_bit_cast(u16x8, dsp[ks]), dqa[db]);
+            for (int i = 0; i < NM; ++i) {
+                if (i + AH < NM) tk[i + AH] = tfrag(kb, u, (i + AH) % DB, (i + AH) / DB);
+                dqa[i % DB] = E::mfma(tk[i], __builtin_bit_cast(u16x8, dsp[i / DB]), dqa[i % DB]);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * AH, 0);
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i < NM - AH) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     auto tile = [&](auto par, int t) {
