@@ -19,6 +19,9 @@ Functions and what pins them (tests/test_oracle.py):
   attn_fwd        plain definition, [P-baidu] §1, §2, §4.1 -- brute force vs a
                   library softmax, invariants, closed forms
   attn_fwd_rows   the same on selected rows -- agreement with attn_fwd
+  attn_fwd_varlen packed variable-length sequences (the padding / varlen
+                  mask kinds of [P-baidu] §8): attn_fwd on every sequence --
+                  a batch of equal lengths against attn_fwd on [B,H,N,d]
   attn_probs      P = Softmax(S) -- rows sum to 1, brute force
   attn_fwd_tiled  block algorithm of [P-baidu] §4.2-§6 -- agreement with
                   attn_fwd at several tile sizes
@@ -313,6 +316,35 @@ def _impl_attn_fwd_masked(lib, q, k, v, dtype, window_left: int, window_right: i
                                       d, int(window_left), int(window_right),
                                       None if sl is None else _ptr(sl), float(scale),
                                       _ptr(o), _ptr(lse)), "oracle_attn_fwd_masked")
+    return o, lse
+
+
+def attn_fwd_varlen(q, k, v, dtype, cu_seqlens, causal: bool, scale: float):
+    """Attention over packed variable-length sequences: q, k, v are uint16
+    bit patterns [H, total, d]; sequence b holds tokens cu_seqlens[b] ..
+    cu_seqlens[b+1]-1 of every head, and attends only within itself (causal
+    or not, top-left aligned).  By definition each sequence is an
+    independent attention problem, so this runs attn_fwd on every
+    (head, sequence) slice.  Returns o [H, total, d] and lse [H, total]
+    (fp64); tokens outside every sequence (after cu_seqlens[-1]) are 0 and
+    -inf."""
+    q, k, v = (np.ascontiguousarray(x, dtype=np.uint16) for x in (q, k, v))
+    if q.ndim != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [H, total, d] shape")
+    H, total, d = q.shape
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu.ndim != 1 or cu.size < 1 or cu[0] != 0 or np.any(np.diff(cu) < 0) or cu[-1] > total:
+        raise ValueError("cu_seqlens must rise from 0 to at most total")
+    o = np.zeros((H, total, d), dtype=np.float64)
+    lse = np.full((H, total), -np.inf, dtype=np.float64)
+    for b in range(cu.size - 1):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        if hi == lo:
+            continue
+        sl = lambda x: np.ascontiguousarray(x[:, lo:hi, :][None])
+        ob, lb = attn_fwd(sl(q), sl(k), sl(v), dtype, causal, scale)
+        o[:, lo:hi, :] = ob[0]
+        lse[:, lo:hi] = lb[0]
     return o, lse
 
 

@@ -18,7 +18,7 @@ import pytest
 import torch
 
 from io_aware_transformer_amd.inputs import bits, make_qkv, WORKLOADS
-from tests.oracle_pins import (PINS, python_reference, run_pins, to_tensor,
+from tests.oracle_pins import (PINS, _qkv, python_reference, run_pins, to_tensor,
                                torch_reference)
 
 
@@ -507,3 +507,43 @@ def test_planted_mistake_is_caught(oracle_source, tmp_path, old, new, what):
     lib = oracle.build(src=src, out=tmp_path / "libmutant.so")
     failed = run_pins(oracle.Oracle(lib))
     assert failed, f"planted mistake '{what}' passed every pin"
+
+
+# ---------------------------------------------------------------- varlen
+
+def test_varlen_equal_lengths_match_batched(oracle_mod):
+    """Packing B equal-length sequences into [H, total, d] must give what the
+    batched [B,H,N,d] attention gives, element for element."""
+    import oracle
+    B, H, N, d = 3, 2, 37, 8
+    q, k, v = _qkv(B, H, N, d, "bf16", seed=71)
+    for causal in (False, True):
+        ro, rl = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), "bf16", causal, 0.3)
+        pack = lambda t: bits(t).transpose(1, 0, 2, 3).reshape(H, B * N, d)
+        o, lse = oracle.attn_fwd_varlen(pack(q), pack(k), pack(v), "bf16",
+                                        [0, N, 2 * N, 3 * N], causal, 0.3)
+        assert np.array_equal(o, ro.transpose(1, 0, 2, 3).reshape(H, B * N, d))
+        assert np.array_equal(lse, rl.transpose(1, 0, 2).reshape(H, B * N))
+
+
+def test_varlen_ragged_and_empty():
+    """A sequence sees only its own keys (a cross-sequence key would change
+    its rows); empty sequences and trailing tokens are left at 0 / -inf."""
+    import oracle
+    H, total, d = 2, 50, 8
+    q, k, v = (bits(t)[0] for t in _qkv(1, H, total, d, "f16", seed=72))
+    cu = [0, 5, 5, 30, 44]
+    o, lse = oracle.attn_fwd_varlen(q, k, v, "f16", cu, True, 0.4)
+    for lo, hi in zip(cu[:-1], cu[1:]):
+        if hi > lo:
+            ro, rl = oracle.attn_fwd(q[None, :, lo:hi], k[None, :, lo:hi], v[None, :, lo:hi],
+                                     "f16", True, 0.4)
+            assert np.array_equal(o[:, lo:hi], ro[0]) and np.array_equal(lse[:, lo:hi], rl[0])
+    assert np.all(o[:, 44:] == 0) and np.all(np.isneginf(lse[:, 44:]))
+    # the first token of each sequence attends only itself: o = v
+    for lo in (0, 5, 30):
+        assert np.allclose(o[:, lo], oracle.decode(v[:, lo], "f16"), rtol=0, atol=1e-15)
+    with pytest.raises(ValueError):
+        oracle.attn_fwd_varlen(q, k, v, "f16", [0, 10, 5], False, 0.4)
+    with pytest.raises(ValueError):
+        oracle.attn_fwd_varlen(q, k, v, "f16", [1, 10], False, 0.4)
