@@ -10,6 +10,7 @@ to stderr.
                   [--workload n8k_causal_peaky] [--secondary n4k_causal]
                   [--backward n8k_causal_peaky] [--window n8k_causal_peaky:1023:0]
                   [--split n4k_h4_causal:4] [--dropout n8k_causal_peaky:0.1]
+                  [--varlen 32:128:8:512:8192]
                   [--no-cold] [--no-cpu-baseline] [--mode copy]
 
 The headline workload is B=1 H=32 N=8192 d=128 bf16 causal with Q,K x3;
@@ -18,7 +19,9 @@ pass (fa_bwd) of the headline workload under "backward", and a sliding-window
 forward (fa_fwd_window, each query sees the 1024 keys ending at itself) under
 "window", and fa_fwd against fa_fwd_split on a few-head shape under "split", and
 the dropout forward and backward (fa_fwd_dropout, fa_bwd_dropout, p = 0.1) of the
-headline workload under "dropout", and the headline forward with cold caches
+headline workload under "dropout", a causal bf16 forward over 8 packed sequences of
+seeded lengths in [512, 8192] (fa_fwd_varlen, 32 heads) under "varlen", and the
+headline forward with cold caches
 (a 512 MB buffer overwritten before each launch) under "cold".  FLOP =
 4*B*H*N^2*d, halved when causal (backward: 2.5 times that).
 """
@@ -238,6 +241,34 @@ def time_split(w, num_splits: int, steps: int, warmup: int, seed: int = 0):
     return out
 
 
+def time_varlen(H: int, d: int, n_seq: int, lo: int, hi: int, steps: int, warmup: int):
+    """fa_fwd_varlen (causal, bf16) on n_seq packed sequences of seeded
+    lengths in [lo, hi]; FLOP = sum over sequences of 2*H*L^2*d."""
+    import torch
+    import io_aware_transformer_amd as fa
+    from io_aware_transformer_amd.inputs import make_qkv, varlen_offsets
+
+    cu = varlen_offsets(n_seq, lo, hi, seed=0)
+    total, lens = cu[-1], [b - a for a, b in zip(cu[:-1], cu[1:])]
+    dev = torch.device("cuda", 0)
+    q, k, v = (t[0].to(dev) for t in make_qkv(1, H, total, d, "bf16", seed=0))
+    o = torch.empty_like(q)
+    lse = torch.empty((H, total), dtype=torch.float32, device=dev)
+    cud = torch.tensor(cu, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    scale = d ** -0.5
+
+    def launch():
+        st = fa.fa_fwd_varlen(q, k, v, o, lse, cud, n_seq, H, total, max(lens), d, 1, scale,
+                              fa.FA_DTYPE_BF16, stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    per = event_times(launch, stream, steps, warmup)
+    flop = sum(2.0 * H * n * n * d for n in lens)
+    return {"lens": lens, "total": total, "ms_mean": sum(per) / len(per), "flop": flop}
+
+
 def time_cold(w, steps: int, seed: int = 0):
     """fa_fwd with the caches cold: before each timed launch a 512 MB buffer
     (twice the 256 MB MALL, far above the L2s) is overwritten on the same
@@ -436,6 +467,9 @@ def main() -> int:
     ap.add_argument("--dropout", default="n8k_causal_peaky:0.1",
                     help="WORKLOAD:P dropout forward and backward reported beside "
                          "('none' to skip)")
+    ap.add_argument("--varlen", default="32:128:8:512:8192",
+                    help="H:d:SEQS:MIN:MAX packed variable-length causal forward reported "
+                         "beside ('none' to skip)")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache timing of the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -566,6 +600,17 @@ def main() -> int:
                          "ms_fa_fwd_split": round(rs["fa_fwd_split"], 5),
                          "tflops_fa_fwd": round(tp, 2), "tflops_fa_fwd_split": round(ts, 2),
                          "frac_fa_fwd_split": round(ts / PEAK_BF16_TFLOPS, 4)}
+
+    if args.varlen and args.varlen != "none":
+        vh, vd, vn, vlo, vhi = (int(x) for x in args.varlen.split(":"))
+        rv = time_varlen(vh, vd, vn, vlo, vhi, args.steps, args.warmup)
+        tv = rv["flop"] / (rv["ms_mean"] * 1e-3) / 1e12
+        log(f"bench: varlen H{vh} d{vd} causal bf16, lengths {rv['lens']}: "
+            f"{rv['ms_mean']*1e3:.1f} us, {tv:.1f} TFLOP/s")
+        line["varlen"] = {"H": vh, "d": vd, "dtype": "bf16", "causal": True,
+                          "lengths": rv["lens"], "total_tokens": rv["total"],
+                          "flop_per_step": rv["flop"], "ms_mean": round(rv["ms_mean"], 5),
+                          "tflops": round(tv, 2), "frac": round(tv / PEAK_BF16_TFLOPS, 4)}
 
     if args.dropout and args.dropout != "none":
         dname, pd = args.dropout.split(":")

@@ -99,6 +99,33 @@ fa_status fa_fwd_window(const void *q, const void *k, const void *v, void *o,
                         int window_right, const int *seqlens, float scale,
                         fa_dtype dtype, hipStream_t stream);
 
+/* Forward pass over packed variable-length sequences, the padding mask kind
+ * of "FlashAttention 优化原理与实现要点解析" §8 with the padding removed:
+ * B sequences of different lengths are stored back to back along the token
+ * axis and each attends only to itself.
+ *   q, k, v, o   [H, total, d] 16-bit (element (h, t, c) at (h*total+t)*d+c)
+ *   lse          [H, total] fp32
+ *   cu_seqlens   device int32 [B + 1]: sequence b is tokens
+ *                cu_seqlens[b] .. cu_seqlens[b+1]-1 of every head; the caller
+ *                guarantees 0 = cu_seqlens[0] <= cu_seqlens[1] <= ... <=
+ *                cu_seqlens[B] <= total and every length <= max_seqlen
+ *   max_seqlen   the longest sequence (1 .. total); it sizes the grid
+ *   causal       0 = every key of the sequence, 1 = keys t' <= t within it
+ *                (each sequence top-left aligned)
+ * Within sequence b this is fa_fwd on its rows.  o and lse rows of tokens
+ * outside every sequence (cu_seqlens[B] .. total-1) are not written.  The
+ * kernel clamps the bounds it reads to [0, total] and each length to the
+ * grid (ceil(max_seqlen / 256) 256-row blocks), so a malformed cu_seqlens
+ * gives wrong rows, never an access outside the tensors.  Other arguments
+ * and errors as fa_fwd: FA_ERR_INVALID_ARG also for a null cu_seqlens,
+ * total < 1, max_seqlen outside 1 .. total, or cu_seqlens overlapping o or
+ * lse; FA_ERR_UNSUPPORTED for max_seqlen > FA_MAX_N; FA_ERR_MISALIGNED for
+ * cu_seqlens not 4-byte aligned.  cu_seqlens is only read. */
+fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o,
+                        float *lse, const int *cu_seqlens, int B, int H, int total,
+                        int max_seqlen, int d, int causal, float scale, fa_dtype dtype,
+                        hipStream_t stream);
+
 /* Most key segments fa_fwd_split accepts. */
 #define FA_MAX_SPLITS 64
 

@@ -14,6 +14,8 @@ C entry points mirrored here with the same names and argument order:
                 scale, dtype, stream) -> status
   fa_fwd_split(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, ws,
                dtype, stream) -> status
+  fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, total, max_seqlen, d,
+                causal, scale, dtype, stream) -> status
   fa_fwd_split_workspace_size(B, H, N, d, num_splits) -> bytes
   fa_bwd(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale,
          dtype, stream) -> status
@@ -43,7 +45,7 @@ FA_DTYPE_BF16 = 1
 
 EXPORTED = ("fa_fwd_f16", "fa_fwd_bf16", "fa_fwd", "fa_fwd_window", "fa_fwd_split",
             "fa_fwd_split_workspace_size", "fa_status_string", "fa_bwd",
-            "fa_bwd_workspace_size", "fa_fwd_dropout", "fa_bwd_dropout")
+            "fa_bwd_workspace_size", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_varlen")
 FA_MAX_SPLITS = 64
 
 _lib = None
@@ -88,6 +90,8 @@ def load():
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd_workspace_size.argtypes = [i, i, i]
     lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.fa_fwd_varlen.argtypes = [p, p, p, p, p, p, i, i, i, i, i, i, f, i, p]
+    lib.fa_fwd_varlen.restype = ctypes.c_int
     u64 = ctypes.c_ulonglong
     u32 = ctypes.c_uint
     lib.fa_fwd_dropout.argtypes = sig + [f, u64, u32, i, p]
@@ -142,6 +146,13 @@ def fa_fwd_split(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, ws, dty
     return load().fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
                                int(N), int(d), int(causal), float(scale), int(num_splits),
                                _ptr(ws), int(dtype), _stream(stream))
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, total, max_seqlen, d, causal, scale,
+                  dtype, stream=None) -> int:
+    return load().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                _ptr(cu_seqlens), int(B), int(H), int(total), int(max_seqlen),
+                                int(d), int(causal), float(scale), int(dtype), _stream(stream))
 
 
 def fa_fwd_split_workspace_size(B, H, N, d, num_splits) -> int:

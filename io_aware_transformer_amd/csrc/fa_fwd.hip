@@ -61,8 +61,10 @@
 // One kernel template serves every forward entry point: MODE 0 / 1 (all
 // keys / causal: fa_fwd), 2 (sliding window and valid lengths, the mask
 // kinds of [P-baidu] §8: fa_fwd_window), 3 (one key segment per grid row,
-// merged by fa_fwd_merge_kernel: fa_fwd_split), and the DROP flag on modes
-// 0 / 1 (dropout fused into the kernel, [P-wmrh] §1.2: fa_fwd_dropout).
+// merged by fa_fwd_merge_kernel: fa_fwd_split), 4 / 5 (all keys / causal
+// over packed variable-length sequences, the padding kind of [P-baidu] §8
+// without the padding: fa_fwd_varlen), and the DROP flag on modes 0 / 1
+// (dropout fused into the kernel, [P-wmrh] §1.2: fa_fwd_dropout).
 // Each variant is a compile-time instantiation, so the tuned full and causal
 // kernels carry none of the others' code.
 
@@ -255,7 +257,12 @@ struct DropArgs {
 // (y = blockIdx.y) of the window rule with L_b = N; writes the segment's
 // normalised O in fp32 to PO and its lse to PL ([y][b*H+h][row]), rows
 // without keys in the segment 0 and -inf, for a merge kernel to combine.
-// Modes 0 and 1 ignore H, wl, wr, LENS, kseg, PO, PL.
+// Modes 0 and 1 ignore H, wl, wr, LENS, kseg, PO, PL.  4 / 5: modes 0 / 1
+// over packed variable-length sequences: N is the token count of each head
+// ([H, N, d] tensors), LENS the cumulative sequence starts (B + 1 values),
+// BH = B*H, and work-group (b*H + h, Q block) works on sequence b of head h,
+// rows [LENS[b], LENS[b+1]) of the head (bounds clamped to [0, N] and the
+// length to nqb Q blocks, so no access leaves the tensors).
 //
 // DROP (modes 0 and 1 only): dropout on the normalised weights.  Weight
 // (b*H+h, i, j) is kept when byte 4*((j%32)/8) + j%4 of Philox4x32-10 with
@@ -269,14 +276,15 @@ template <int DT, int D, int MODE, bool DROP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                    const u16 *__restrict__ V, u16 *__restrict__ O,
-                   float *__restrict__ LSE, int BH, int N, int nqb, float c,
+                   float *__restrict__ LSE, int BH, int N_in, int nqb, float c,
                    unsigned qand, unsigned qxor, int H, int wl, int wr,
                    const int *__restrict__ LENS, int kseg, float *__restrict__ PO,
                    float *__restrict__ PL, DropArgs dr)
 {
     static_assert(!DROP || MODE <= 1, "dropout is built for the full and causal masks");
-    constexpr bool CAUSAL = MODE == 1;
-    constexpr bool GEN = MODE >= 2;
+    constexpr bool VARLEN = MODE >= 4;
+    constexpr bool CAUSAL = MODE == 1 || MODE == 5;
+    constexpr bool GEN = MODE == 2 || MODE == 3;
     constexpr bool SPLIT = MODE == 3;
     // the fp32 row sum is kept for bfloat16 and under dropout (where the
     // weights applied to V no longer sum to the normaliser)
@@ -314,7 +322,19 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     const int L = blockIdx.x;
     const int bh = L % BH;
     const int qblk = CAUSAL ? (nqb - 1 - L / BH) : (L / BH);
-    const size_t head = (size_t)bh * (size_t)N * D;
+    // N: rows of this work-group's attention problem; row0: its first row in
+    // the [rows, d] view of the tensors
+    int N = N_in;
+    size_t row0 = (size_t)bh * (size_t)N_in;
+    if constexpr (VARLEN) {
+        const int b = bh / H, h = bh % H;
+        const int start = min(max(LENS[b], 0), N_in);
+        const int end = min(max(LENS[b + 1], start), N_in);
+        N = min(end - start, nqb * kBR);
+        row0 = (size_t)h * (size_t)N_in + (size_t)start;
+        if (qblk * kBR >= N) return;                   // Q block past the sequence
+    }
+    const size_t head = row0 * D;
     const int nbytes = N * T::kRowBytes;
     const __amdgpu_buffer_rsrc_t rq =
         __builtin_amdgcn_make_buffer_rsrc((void *)(Q + head), 0, nbytes, kRsrcWord3);
@@ -365,7 +385,7 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) *(u32x2 *)(orow + 32 * db + 8 * g + 4 * hh) = z;
-            if (hh == 0) LSE[(size_t)bh * N + qrow] = neg_inf();
+            if (hh == 0) LSE[row0 + qrow] = neg_inf();
         }
     };
     if constexpr (GEN) {
@@ -724,7 +744,7 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                     *(u32x2 *)(orow + 32 * db + 8 * g + 4 * hh) = pr;
                 }
             if (hh == 0)
-                LSE[(size_t)bh * N + qrow] = (m + log2f(lt)) * 0.69314718055994530942f;
+                LSE[row0 + qrow] = (m + log2f(lt)) * 0.69314718055994530942f;
         }
     }
 }
@@ -741,7 +761,9 @@ kernel_fn pick_d(int mode, bool drop)
     case 0: return fa_fwd_kernel<DT, D, 0, false>;
     case 1: return fa_fwd_kernel<DT, D, 1, false>;
     case 2: return fa_fwd_kernel<DT, D, 2, false>;
-    default: return fa_fwd_kernel<DT, D, 3, false>;
+    case 3: return fa_fwd_kernel<DT, D, 3, false>;
+    case 4: return fa_fwd_kernel<DT, D, 4, false>;
+    default: return fa_fwd_kernel<DT, D, 5, false>;
     }
 }
 
@@ -837,12 +859,14 @@ fa_status launch_fwd(const void *q, const void *k, const void *v, void *o, float
                      int H, int N, int d, int mode, int wl, int wr, const int *lens,
                      float scale, fa_dtype dtype, hipStream_t stream, int nseg = 1,
                      int kseg = 0, float *po = nullptr, float *pl = nullptr,
-                     const DropArgs *drop = nullptr)
+                     const DropArgs *drop = nullptr, int max_rows = 0)
 {
-    const fa_status vs = validate_fwd(q, k, v, o, lse, B, H, N, d, lens, scale, dtype);
-    if (vs != FA_OK) return vs;
+    if (mode < 4) {
+        const fa_status vs = validate_fwd(q, k, v, o, lse, B, H, N, d, lens, scale, dtype);
+        if (vs != FA_OK) return vs;
+    }
     const long long BH = (long long)B * H;
-    const long long nqb = (N + kBR - 1) / kBR;
+    const long long nqb = ((mode >= 4 ? max_rows : N) + kBR - 1) / kBR;
     const long long grid = BH * nqb;
     if (drop && mode > 1) return FA_ERR_INVALID_ARG;
     kernel_fn fn = (dtype == FA_DTYPE_F16) ? pick<FA_DTYPE_F16>(d, mode, drop != nullptr)
@@ -969,6 +993,37 @@ extern "C" fa_status fa_fwd_dropout(const void *q, const void *k, const void *v,
                          thr ? 256.f / (float)thr : 0.f};
     return launch_fwd(q, k, v, o, lse, B, H, N, d, causal, -1, causal ? 0 : -1, nullptr, scale,
                       dtype, stream, 1, 0, nullptr, nullptr, &dr);
+}
+
+extern "C" fa_status fa_fwd_varlen(const void *q, const void *k, const void *v, void *o,
+                                   float *lse, const int *cu_seqlens, int B, int H, int total,
+                                   int max_seqlen, int d, int causal, float scale,
+                                   fa_dtype dtype, hipStream_t stream)
+{
+    if (!q || !k || !v || !o || !lse || !cu_seqlens) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || total < 1 || max_seqlen < 1 || max_seqlen > total)
+        return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (max_seqlen > FA_MAX_N) return FA_ERR_UNSUPPORTED;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
+        return FA_ERR_MISALIGNED;
+    if (((uintptr_t)lse | (uintptr_t)cu_seqlens) & 3) return FA_ERR_MISALIGNED;
+    const long long BH = (long long)B * H;
+    const long long grid = BH * ((max_seqlen + kBR - 1) / kBR);
+    if (BH > INT_MAX || grid > INT_MAX) return FA_ERR_INVALID_ARG;
+    const size_t tb = (size_t)H * (size_t)total * (size_t)d * 2;
+    const size_t lb = (size_t)H * (size_t)total * 4, cb = ((size_t)B + 1) * 4;
+    if (overlaps(o, tb, q, tb) || overlaps(o, tb, k, tb) || overlaps(o, tb, v, tb) ||
+        overlaps(lse, lb, q, tb) || overlaps(lse, lb, k, tb) || overlaps(lse, lb, v, tb) ||
+        overlaps(lse, lb, o, tb) || overlaps(o, tb, cu_seqlens, cb) ||
+        overlaps(lse, lb, cu_seqlens, cb))
+        return FA_ERR_INVALID_ARG;
+    return launch_fwd(q, k, v, o, lse, B, H, total, d, causal ? 5 : 4, -1, causal ? 0 : -1,
+                      cu_seqlens, scale, dtype, stream, 1, 0, nullptr, nullptr, nullptr,
+                      max_seqlen);
 }
 
 extern "C" fa_status fa_fwd_f16(const void *q, const void *k, const void *v, void *o,

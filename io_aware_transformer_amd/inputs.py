@@ -93,6 +93,13 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0,
     return q.to(t), k.to(t), v.to(t)
 
 
+def varlen_offsets(n_seq: int, lo: int, hi: int, seed: int = 0):
+    """Cumulative starts [0, L_0, L_0+L_1, ...] of n_seq packed sequences
+    with lengths drawn uniformly from [lo, hi] by a seeded numpy generator."""
+    lens = np.random.default_rng(seed).integers(lo, hi + 1, size=n_seq)
+    return [0] + np.cumsum(lens).astype(int).tolist()
+
+
 def make_workload(w: Workload, seed: int = 0):
     return make_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=seed, qk_gain=w.qk_gain)
 

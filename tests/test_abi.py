@@ -262,3 +262,30 @@ def test_dropout_bwd_unsupported_and_misaligned():
     assert dbcall(d=256) == fa.FA_ERR_UNSUPPORTED
     assert dbcall(dk=DK + 8) == fa.FA_ERR_MISALIGNED
     assert dbcall(ws=WS + 4) == fa.FA_ERR_MISALIGNED
+
+
+# ---------------------------------------------------------------- packed varlen
+
+CU = 0x10000 * 14
+
+
+def vcall(q=Q, k=K, v=V, o=O, lse=L, cu=CU, B=2, H=1, total=64, maxlen=40, d=128, causal=0,
+          scale=0.125, dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_fwd_varlen(q, k, v, o, lse, cu, B, H, total, maxlen, d, causal, scale, dtype,
+                            None)
+
+
+@pytest.mark.parametrize("kw", [dict(cu=0), dict(q=0), dict(lse=0), dict(B=0), dict(H=0),
+                                dict(total=0), dict(maxlen=0), dict(maxlen=65), dict(causal=2),
+                                dict(scale=math.inf), dict(dtype=2), dict(o=Q + 16),
+                                dict(cu=O + 64), dict(lse=CU)])
+def test_varlen_invalid(kw):
+    assert vcall(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_varlen_unsupported_and_misaligned():
+    assert vcall(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert vcall(total=(1 << 22) + 2, maxlen=(1 << 22) + 1, q=1 << 40, k=2 << 40, v=3 << 40,
+                 o=4 << 40, lse=5 << 40, cu=6 << 40) == fa.FA_ERR_UNSUPPORTED
+    assert vcall(cu=CU + 2) == fa.FA_ERR_MISALIGNED
+    assert vcall(v=V + 8) == fa.FA_ERR_MISALIGNED
