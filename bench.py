@@ -478,9 +478,9 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
-              "supported (the forward pass shards over heads without communication, "
-              "so per-GPU throughput is the one-GPU figure).", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported (the "
+              "forward pass shards over heads without communication, so per-GPU "
+              "throughput is the one-GPU figure).", file=sys.stderr)
         return 2
     if args.mode == "copy":
         copy_mode(args.steps)
