@@ -129,3 +129,13 @@ def test_varlen_malformed_offsets_stay_in_bounds():
     o, lse = gpu_varlen(q, k, v, [0, 150, 90, 5000], 200, False, 0.125)
     torch.cuda.synchronize()
     assert torch.isfinite(o[:, :150]).all()
+
+
+def test_varlen_benchmarked_launch():
+    """The launch bench.py times: 8 sequences of seeded lengths in [512, 8192]
+    (24 900 tokens), 32 heads, d128 bf16 causal, every row compared."""
+    from io_aware_transformer_amd.inputs import varlen_offsets
+    cu = varlen_offsets(8, 512, 8192, seed=0)
+    note(f"[varlen parity] benchmarked launch cu={cu}")
+    q, k, v = packed(32, cu[-1], 128, "bf16", seed=0)
+    check(q, k, v, cu, True, float(np.float32(128 ** -0.5)))
