@@ -22,6 +22,8 @@ Functions and what pins them (tests/test_oracle.py):
   attn_fwd_varlen packed variable-length sequences (the padding / varlen
                   mask kinds of [P-baidu] §8): attn_fwd on every sequence --
                   a batch of equal lengths against attn_fwd on [B,H,N,d]
+  attn_bwd_varlen its gradients: attn_bwd (given o) on every sequence -- the
+                  same batched comparison
   attn_probs      P = Softmax(S) -- rows sum to 1, brute force
   attn_fwd_tiled  block algorithm of [P-baidu] §4.2-§6 -- agreement with
                   attn_fwd at several tile sizes
@@ -346,6 +348,31 @@ def attn_fwd_varlen(q, k, v, dtype, cu_seqlens, causal: bool, scale: float):
         o[:, lo:hi, :] = ob[0]
         lse[:, lo:hi] = lb[0]
     return o, lse
+
+
+def attn_bwd_varlen(q, k, v, do, o, dtype, cu_seqlens, causal: bool, scale: float):
+    """Gradients of attn_fwd_varlen for an upstream do, with the row term
+    from the given 16-bit o (as attn_bwd(..., o=...)): every sequence is an
+    independent problem, so this runs attn_bwd on every (head, sequence)
+    slice.  All arrays [H, total, d]; rows outside every sequence get 0."""
+    arrs = [np.ascontiguousarray(x, dtype=np.uint16) for x in (q, k, v, do, o)]
+    q, k, v, do, o = arrs
+    if q.ndim != 3 or any(x.shape != q.shape for x in arrs):
+        raise ValueError("q, k, v, do, o must share one [H, total, d] shape")
+    H, total, d = q.shape
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu.ndim != 1 or cu.size < 1 or cu[0] != 0 or np.any(np.diff(cu) < 0) or cu[-1] > total:
+        raise ValueError("cu_seqlens must rise from 0 to at most total")
+    grads = [np.zeros((H, total, d), dtype=np.float64) for _ in range(3)]
+    for b in range(cu.size - 1):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        if hi == lo:
+            continue
+        sl = lambda x: np.ascontiguousarray(x[:, lo:hi, :][None])
+        gb = attn_bwd(sl(q), sl(k), sl(v), sl(do), dtype, causal, scale, o=sl(o))
+        for g, x in zip(grads, gb):
+            g[:, lo:hi, :] = x[0]
+    return tuple(grads)
 
 
 def dropout_threshold(p_drop: float) -> int:

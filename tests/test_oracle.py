@@ -547,3 +547,30 @@ def test_varlen_ragged_and_empty():
         oracle.attn_fwd_varlen(q, k, v, "f16", [0, 10, 5], False, 0.4)
     with pytest.raises(ValueError):
         oracle.attn_fwd_varlen(q, k, v, "f16", [1, 10], False, 0.4)
+
+
+def test_varlen_bwd_equal_lengths_match_batched(oracle_mod):
+    import oracle
+    B, H, N, d = 3, 2, 23, 8
+    q, k, v = _qkv(B, H, N, d, "f16", seed=73)
+    do = _qkv(B, H, N, d, "f16", seed=74)[0]
+    o16 = _qkv(B, H, N, d, "f16", seed=75)[0]       # any 16-bit o: the row term uses it
+    pack = lambda t: bits(t).transpose(1, 0, 2, 3).reshape(H, B * N, d)
+    for causal in (False, True):
+        ref = oracle_mod.attn_bwd(bits(q), bits(k), bits(v), bits(do), "f16", causal, 0.3,
+                                  o=bits(o16))
+        got = oracle.attn_bwd_varlen(pack(q), pack(k), pack(v), pack(do), pack(o16), "f16",
+                                     [0, N, 2 * N, 3 * N], causal, 0.3)
+        for g, r in zip(got, ref):
+            assert np.array_equal(g, r.transpose(1, 0, 2, 3).reshape(H, B * N, d))
+    # ragged with an empty sequence and trailing tokens
+    H, total = 1, 40
+    q, k, v, do, o = (bits(t)[0] for t in (_qkv(1, H, total, d, "bf16", seed=76) +
+                                            _qkv(1, H, total, d, "bf16", seed=77)[:2]))
+    g = oracle.attn_bwd_varlen(q, k, v, do, o, "bf16", [0, 9, 9, 31], True, 0.5)
+    for x in g:
+        assert np.all(x[:, 31:] == 0)
+    r = oracle_mod.attn_bwd(q[None, :, 9:31], k[None, :, 9:31], v[None, :, 9:31],
+                            do[None, :, 9:31], "bf16", True, 0.5, o=o[None, :, 9:31])
+    for x, y in zip(g, r):
+        assert np.array_equal(x[:, 9:31], y[0])
