@@ -19,10 +19,10 @@ pass (fa_bwd) of the headline workload under "backward", and a sliding-window
 forward (fa_fwd_window, each query sees the 1024 keys ending at itself) under
 "window", and fa_fwd against fa_fwd_split on a few-head shape under "split", and
 the dropout forward and backward (fa_fwd_dropout, fa_bwd_dropout, p = 0.1) of the
-headline workload under "dropout", a causal bf16 forward over 8 packed sequences of
-seeded lengths in [512, 8192] (fa_fwd_varlen, 32 heads) under "varlen", and the
-headline forward with cold caches
-(a 512 MB buffer overwritten before each launch) under "cold".  FLOP =
+headline workload under "dropout", a causal bf16 forward and backward over 8
+packed sequences of seeded lengths in [512, 8192] (fa_fwd_varlen, fa_bwd_varlen,
+32 heads) under "varlen", and the headline forward with cold caches (a 512 MB
+buffer overwritten before each launch) under "cold".  FLOP =
 4*B*H*N^2*d, halved when causal (backward: 2.5 times that).
 """
 from __future__ import annotations
@@ -243,7 +243,8 @@ def time_split(w, num_splits: int, steps: int, warmup: int, seed: int = 0):
 
 def time_varlen(H: int, d: int, n_seq: int, lo: int, hi: int, steps: int, warmup: int):
     """fa_fwd_varlen (causal, bf16) on n_seq packed sequences of seeded
-    lengths in [lo, hi]; FLOP = sum over sequences of 2*H*L^2*d."""
+    lengths in [lo, hi], then fa_bwd_varlen on its (o, lse) and a seeded dO;
+    forward FLOP = sum over sequences of 2*H*L^2*d (backward: 2.5 times)."""
     import torch
     import io_aware_transformer_amd as fa
     from io_aware_transformer_amd.inputs import make_qkv, varlen_offsets
@@ -266,7 +267,21 @@ def time_varlen(H: int, d: int, n_seq: int, lo: int, hi: int, steps: int, warmup
 
     per = event_times(launch, stream, steps, warmup)
     flop = sum(2.0 * H * n * n * d for n in lens)
-    return {"lens": lens, "total": total, "ms_mean": sum(per) / len(per), "flop": flop}
+
+    do = make_qkv(1, H, total, d, "bf16", seed=12345)[0][0].to(dev)
+    ws = torch.empty(fa.fa_bwd_varlen_workspace_size(n_seq, H, total) // 4,
+                     dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+
+    def backward():
+        st = fa.fa_bwd_varlen(q, k, v, o, do, lse, cud, ws, dq, dk, dv, n_seq, H, total,
+                              max(lens), d, 1, scale, fa.FA_DTYPE_BF16, stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    per_b = event_times(backward, stream, steps, warmup)
+    return {"lens": lens, "total": total, "ms_mean": sum(per) / len(per), "flop": flop,
+            "bwd_ms_mean": sum(per_b) / len(per_b)}
 
 
 def time_cold(w, steps: int, seed: int = 0):
@@ -605,12 +620,17 @@ def main() -> int:
         vh, vd, vn, vlo, vhi = (int(x) for x in args.varlen.split(":"))
         rv = time_varlen(vh, vd, vn, vlo, vhi, args.steps, args.warmup)
         tv = rv["flop"] / (rv["ms_mean"] * 1e-3) / 1e12
+        tvb = 2.5 * rv["flop"] / (rv["bwd_ms_mean"] * 1e-3) / 1e12
         log(f"bench: varlen H{vh} d{vd} causal bf16, lengths {rv['lens']}: "
-            f"{rv['ms_mean']*1e3:.1f} us, {tv:.1f} TFLOP/s")
+            f"{rv['ms_mean']*1e3:.1f} us, {tv:.1f} TFLOP/s; backward "
+            f"{rv['bwd_ms_mean']*1e3:.1f} us, {tvb:.1f} TFLOP/s")
         line["varlen"] = {"H": vh, "d": vd, "dtype": "bf16", "causal": True,
                           "lengths": rv["lens"], "total_tokens": rv["total"],
                           "flop_per_step": rv["flop"], "ms_mean": round(rv["ms_mean"], 5),
-                          "tflops": round(tv, 2), "frac": round(tv / PEAK_BF16_TFLOPS, 4)}
+                          "tflops": round(tv, 2), "frac": round(tv / PEAK_BF16_TFLOPS, 4),
+                          "bwd_ms_mean": round(rv["bwd_ms_mean"], 5),
+                          "bwd_tflops": round(tvb, 2),
+                          "bwd_frac": round(tvb / PEAK_BF16_TFLOPS, 4)}
 
     if args.dropout and args.dropout != "none":
         dname, pd = args.dropout.split(":")

@@ -82,6 +82,35 @@ fa_status fa_bwd_dropout(const void *q, const void *k, const void *v, const void
                          float p_drop, unsigned long long seed, unsigned offset,
                          fa_dtype dtype, hipStream_t stream);
 
+/* Bytes of fp32 workspace fa_bwd_varlen needs (0 if a size is not
+ * positive): per head, 32 * (ceil(total / 32) + B) rows of (lse, D). */
+size_t fa_bwd_varlen_workspace_size(int B, int H, int total);
+
+/* Backward pass of fa_fwd_varlen: within every packed sequence b (tokens
+ * cu_seqlens[b] .. cu_seqlens[b+1]-1 of every head), the gradients fa_bwd
+ * computes for that sequence alone, as if it were a [1,1,L_b,d] problem.
+ *   q, k, v, o, dO  [H, total, d] 16-bit (o and lse as fa_fwd_varlen wrote
+ *                   them for the same q, k, v, cu_seqlens, causal, scale),
+ *                   read only
+ *   lse             [H, total] fp32, read only
+ *   cu_seqlens      device int32 [B + 1], the contract of fa_fwd_varlen
+ *   ws              fa_bwd_varlen_workspace_size(B, H, total) bytes,
+ *                   16-byte aligned, scratch
+ *   dq, dk, dv      [H, total, d] 16-bit, written for every token inside a
+ *                   sequence; rows of tokens outside every sequence
+ *                   (cu_seqlens[B] .. total-1) are not written
+ *   max_seqlen      the longest sequence (1 .. total); it sizes the grids
+ * Bounds and lengths are clamped as in fa_fwd_varlen, so a malformed
+ * cu_seqlens gives wrong rows, never an access outside the tensors or the
+ * workspace.  Errors as fa_bwd, plus those fa_fwd_varlen adds for
+ * cu_seqlens, total and max_seqlen.  Three kernels are enqueued on
+ * `stream`; results are deterministic. */
+fa_status fa_bwd_varlen(const void *q, const void *k, const void *v, const void *o,
+                        const void *dO, const float *lse, const int *cu_seqlens, float *ws,
+                        void *dq, void *dk, void *dv, int B, int H, int total,
+                        int max_seqlen, int d, int causal, float scale, fa_dtype dtype,
+                        hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -168,6 +168,34 @@ struct DropArgs {
     float fscale;
 };
 
+// Packed variable-length sequences (VARLEN kernels): tensors [H, total, d],
+// sequence b of head h is rows cu[b] .. cu[b+1]-1 of the head (bounds
+// clamped to [0, total], length to cap rows).  Its workspace rows start at
+// 32 * (ceil(cu[b] / 32) + b) of the head's wsh rows, so sequences never
+// share a 32-row workspace block.
+struct VarlenArgs {
+    const int *cu;
+    int H, cap, wsh;
+};
+
+// This work-group's sequence: rows, first row in the [H*total, d] view,
+// first workspace row.
+struct Seq {
+    int n;
+    size_t row0, ws_row0;
+};
+__device__ __forceinline__ Seq varlen_seq(const VarlenArgs &vl, int bh, int total)
+{
+    const int b = bh / vl.H, h = bh % vl.H;
+    const int start = min(max(vl.cu[b], 0), total);
+    const int end = min(max(vl.cu[b + 1], start), total);
+    Seq s;
+    s.n = min(end - start, vl.cap);
+    s.row0 = (size_t)h * (size_t)total + (size_t)start;
+    s.ws_row0 = (size_t)h * (size_t)vl.wsh + 32 * ((size_t)((start + 31) / 32) + (size_t)b);
+    return s;
+}
+
 // Byte transpose of a 4x4 byte matrix held by the 4 lanes of a quad (lane e
 // holds row e as one word): afterwards lane e holds column e.  Two stages:
 // swap 16-bit halves with lane e^2, then bytes with lane e^1 (DPP quad
@@ -239,6 +267,44 @@ void fa_bwd_delta_kernel(const u16 *__restrict__ O, const u16 *__restrict__ dO,
     }
 }
 
+// The same for packed sequences: grid (row chunk, b*H + h); rows of the
+// sequence's last 32-row workspace block past its length get (+inf, 0).
+template <int DT, int D>
+__global__ __launch_bounds__(256)
+void fa_bwd_delta_varlen_kernel(const u16 *__restrict__ O, const u16 *__restrict__ dO,
+                                const float *__restrict__ LSE, float *__restrict__ WS, int total,
+                                VarlenArgs vl)
+{
+    using E = Elem<DT>;
+    constexpr int LPR = D / 8;
+    constexpr int RPB = 256 / LPR;
+    const Seq sq = varlen_seq(vl, blockIdx.y, total);
+    const int r = blockIdx.x * RPB + threadIdx.x / LPR;    // row within the sequence
+    const int part = threadIdx.x % LPR;
+    const int padded = (sq.n + kWsRows - 1) / kWsRows * kWsRows;
+    const bool valid = r < sq.n;
+    float acc = 0.f;
+    if (valid) {
+        const size_t off = (sq.row0 + r) * D + part * 8;
+        const u32x4 a = *(const u32x4 *)(O + off);
+        const u32x4 b = *(const u32x4 *)(dO + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = fmaf(E::lo(a[e]), E::lo(b[e]), acc);
+            acc = fmaf(E::hi(a[e]), E::hi(b[e]), acc);
+        }
+    }
+#pragma unroll
+    for (int s = LPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s);
+    if (r < padded && part == 0) {
+        const size_t idx = sq.ws_row0 + r;
+        float *blk = WS + idx / kWsRows * (2 * kWsRows);
+        const int i = (int)(idx % kWsRows);
+        blk[i] = valid ? LSE[sq.row0 + r] * kLog2e : __builtin_inff();
+        blk[kWsRows + i] = acc;
+    }
+}
+
 // ---------------------------------------------------------------- dK / dV
 
 // DROP: the dropout of the forward pass, redrawn.  dV^T += dO^T (P o Z) and
@@ -247,14 +313,15 @@ void fa_bwd_delta_kernel(const u16 *__restrict__ O, const u16 *__restrict__ dO,
 // (query qs + l32, key half hh) of each step and the 32 x 32 bytes are
 // transposed through a per-wave LDS block: a byte transpose inside each
 // lane quad, 4 dword writes, and in the step one 16-byte read per lane.
-template <int DT, int D, bool CAUSAL, bool DROP>
+template <int DT, int D, bool CAUSAL, bool DROP, bool VARLEN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                         const u16 *__restrict__ V, const u16 *__restrict__ dO,
                         const float *__restrict__ WS, u16 *__restrict__ dK,
-                        u16 *__restrict__ dV, int BH, int N, int nblk, float c2, float scale,
-                        DropArgs dr)
+                        u16 *__restrict__ dV, int BH, int N_in, int nblk_in, float c2,
+                        float scale, DropArgs dr, VarlenArgs vl)
 {
+    static_assert(!(DROP && VARLEN), "dropout is built for the batched layout");
     using E = Elem<DT>;
     using T = Tile<D>;
     constexpr int KT = D / 16;                 // MFMA k-steps over d
@@ -295,13 +362,25 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     const int L = blockIdx.x;
     const int bh = L % BH;
     const int kb = L / BH;                     // causal: low key blocks (most work) first
-    const size_t head = (size_t)bh * (size_t)N * D;
+    // this work-group's problem: N rows starting at row0 of the [rows, d]
+    // view, workspace blocks from ws_blk0 (nblk of them)
+    int N = N_in, nblk = nblk_in;
+    size_t row0 = (size_t)bh * (size_t)N_in, ws_blk0 = (size_t)bh * nblk_in;
+    if constexpr (VARLEN) {
+        const Seq sq = varlen_seq(vl, bh, N_in);
+        N = sq.n;
+        nblk = (N + kWsRows - 1) / kWsRows;
+        row0 = sq.row0;
+        ws_blk0 = sq.ws_row0 / kWsRows;
+        if (kb * kKeysA >= N) return;          // key block past the sequence
+    }
+    const size_t head = row0 * D;
     const int nbytes = N * T::kRowBytes;
     const __amdgpu_buffer_rsrc_t rq = rsrc(Q + head, nbytes);
     const __amdgpu_buffer_rsrc_t rk = rsrc(K + head, nbytes);
     const __amdgpu_buffer_rsrc_t rv = rsrc(V + head, nbytes);
     const __amdgpu_buffer_rsrc_t rdo = rsrc(dO + head, nbytes);
-    const __amdgpu_buffer_rsrc_t rw = rsrc(WS + (size_t)bh * nblk * (2 * kWsRows), nblk * 2 * kWsRows * 4);
+    const __amdgpu_buffer_rsrc_t rw = rsrc(WS + ws_blk0 * (2 * kWsRows), nblk * 2 * kWsRows * 4);
 
     const int k0 = kb * kKeysA;
     const int kw = k0 + 32 * w;                // this wave's first key
@@ -591,13 +670,14 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
 // DROP: dS = P o (Z o dP - D) with the forward's keep factors Z; a lane
 // holds 16 keys of one query, the 16 bytes of one Philox call per step.
-template <int DT, int D, bool CAUSAL, bool DROP>
+template <int DT, int D, bool CAUSAL, bool DROP, bool VARLEN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                       const u16 *__restrict__ V, const u16 *__restrict__ dO,
-                      const float *__restrict__ WS, u16 *__restrict__ dQ, int BH, int N,
-                      int nblk, int nqb, float c2, float scale, DropArgs dr)
+                      const float *__restrict__ WS, u16 *__restrict__ dQ, int BH, int N_in,
+                      int nblk, int nqb, float c2, float scale, DropArgs dr, VarlenArgs vl)
 {
+    static_assert(!(DROP && VARLEN), "dropout is built for the batched layout");
     using E = Elem<DT>;
     using T = Tile<D>;
     constexpr int KT = D / 16;
@@ -628,7 +708,16 @@ void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     const int L = blockIdx.x;
     const int bh = L % BH;
     const int qblk = CAUSAL ? (nqb - 1 - L / BH) : (L / BH);
-    const size_t head = (size_t)bh * (size_t)N * D;
+    int N = N_in;
+    size_t row0 = (size_t)bh * (size_t)N_in, ws_blk0 = (size_t)bh * nblk;
+    if constexpr (VARLEN) {
+        const Seq sq = varlen_seq(vl, bh, N_in);
+        N = sq.n;
+        row0 = sq.row0;
+        ws_blk0 = sq.ws_row0 / kWsRows;
+        if (qblk * kQB >= N) return;           // Q block past the sequence
+    }
+    const size_t head = row0 * D;
     const int nbytes = N * T::kRowBytes;
     const __amdgpu_buffer_rsrc_t rq = rsrc(Q + head, nbytes);
     const __amdgpu_buffer_rsrc_t rk = rsrc(K + head, nbytes);
@@ -649,7 +738,7 @@ void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     // this lane's row statistics (rows past N read as +inf and 0)
     float l2 = __builtin_inff(), dd = 0.f;
     if (qrow < N) {
-        const float *blk = WS + ((size_t)bh * nblk + qrow / kWsRows) * (2 * kWsRows);
+        const float *blk = WS + (ws_blk0 + qrow / kWsRows) * (2 * kWsRows);
         l2 = blk[qrow % kWsRows];
         dd = blk[kWsRows + qrow % kWsRows];
     }
@@ -831,6 +920,7 @@ hipError_t launch(const void *q, const void *k, const void *v, const void *o, co
                   const float *lse, float *ws, void *dq, void *dk, void *dv, int BH, int N,
                   float scale, DropArgs dr, hipStream_t stream)
 {
+    const VarlenArgs vl = {nullptr, 1, 0, 0};
     const int nblk = (N + kWsRows - 1) / kWsRows;
     const long long rows_padded = (long long)BH * nblk * kWsRows;
     constexpr int RPB = 256 / (D / 8);
@@ -840,15 +930,52 @@ hipError_t launch(const void *q, const void *k, const void *v, const void *o, co
     const float c2 = scale * kLog2e;
     hipLaunchKernelGGL((fa_bwd_delta_kernel<DT, D>), dim3((unsigned)g1), dim3(256), 0, stream,
                        (const u16 *)o, (const u16 *)dO, lse, ws, N, nblk, rows_padded);
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D, CAUSAL, DROP>),
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D, CAUSAL, DROP, false>),
                        dim3((unsigned)((long long)BH * nkb)), dim3(kThreads), 0, stream,
                        (const u16 *)q, (const u16 *)k, (const u16 *)v, (const u16 *)dO,
-                       (const float *)ws, (u16 *)dk, (u16 *)dv, BH, N, nblk, c2, scale, dr);
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<DT, D, CAUSAL, DROP>),
+                       (const float *)ws, (u16 *)dk, (u16 *)dv, BH, N, nblk, c2, scale, dr, vl);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<DT, D, CAUSAL, DROP, false>),
                        dim3((unsigned)((long long)BH * nqb)), dim3(kThreads), 0, stream,
                        (const u16 *)q, (const u16 *)k, (const u16 *)v, (const u16 *)dO,
-                       (const float *)ws, (u16 *)dq, BH, N, nblk, nqb, c2, scale, dr);
+                       (const float *)ws, (u16 *)dq, BH, N, nblk, nqb, c2, scale, dr, vl);
     return hipGetLastError();
+}
+
+// Packed sequences: total rows per head, at most cap (a multiple of 256)
+// rows per sequence.
+template <int DT, int D, bool CAUSAL>
+hipError_t launch_varlen(const void *q, const void *k, const void *v, const void *o,
+                         const void *dO, const float *lse, float *ws, void *dq, void *dk,
+                         void *dv, int BH, int total, VarlenArgs vl, float scale,
+                         hipStream_t stream)
+{
+    constexpr int RPB = 256 / (D / 8);
+    const DropArgs dr = {0u, 0u, 0u, 256u, 1.f};
+    const float c2 = scale * kLog2e;
+    const int nb = vl.cap / kKeysA;            // key blocks = Q blocks per sequence
+    hipLaunchKernelGGL((fa_bwd_delta_varlen_kernel<DT, D>),
+                       dim3((unsigned)((vl.cap + RPB - 1) / RPB), (unsigned)BH), dim3(256), 0,
+                       stream, (const u16 *)o, (const u16 *)dO, lse, ws, total, vl);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D, CAUSAL, false, true>),
+                       dim3((unsigned)((long long)BH * nb)), dim3(kThreads), 0, stream,
+                       (const u16 *)q, (const u16 *)k, (const u16 *)v, (const u16 *)dO,
+                       (const float *)ws, (u16 *)dk, (u16 *)dv, BH, total, 0, c2, scale, dr, vl);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<DT, D, CAUSAL, false, true>),
+                       dim3((unsigned)((long long)BH * nb)), dim3(kThreads), 0, stream,
+                       (const u16 *)q, (const u16 *)k, (const u16 *)v, (const u16 *)dO,
+                       (const float *)ws, (u16 *)dq, BH, total, 0, nb, c2, scale, dr, vl);
+    return hipGetLastError();
+}
+
+typedef hipError_t (*launch_varlen_fn)(const void *, const void *, const void *, const void *,
+                                       const void *, const float *, float *, void *, void *,
+                                       void *, int, int, VarlenArgs, float, hipStream_t);
+
+template <int DT>
+launch_varlen_fn pick_varlen(int d, int causal)
+{
+    if (d == 64) return causal ? launch_varlen<DT, 64, true> : launch_varlen<DT, 64, false>;
+    return causal ? launch_varlen<DT, 128, true> : launch_varlen<DT, 128, false>;
 }
 
 typedef hipError_t (*launch_fn)(const void *, const void *, const void *, const void *,
@@ -950,4 +1077,58 @@ extern "C" fa_status fa_bwd_dropout(const void *q, const void *k, const void *v,
                          thr ? 256.f / (float)thr : 0.f};
     return run_bwd(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale, dtype, &dr,
                    stream);
+}
+
+extern "C" size_t fa_bwd_varlen_workspace_size(int B, int H, int total)
+{
+    if (B < 1 || H < 1 || total < 1) return 0;
+    const size_t wsh = (size_t)kWsRows * ((size_t)(total + kWsRows - 1) / kWsRows + (size_t)B);
+    return (size_t)H * wsh * 2 * sizeof(float);
+}
+
+extern "C" fa_status fa_bwd_varlen(const void *q, const void *k, const void *v, const void *o,
+                                   const void *dO, const float *lse, const int *cu_seqlens,
+                                   float *ws, void *dq, void *dk, void *dv, int B, int H,
+                                   int total, int max_seqlen, int d, int causal, float scale,
+                                   fa_dtype dtype, hipStream_t stream)
+{
+    if (!q || !k || !v || !o || !dO || !lse || !cu_seqlens || !ws || !dq || !dk || !dv)
+        return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || total < 1 || max_seqlen < 1 || max_seqlen > total)
+        return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (max_seqlen > FA_MAX_N) return FA_ERR_UNSUPPORTED;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dO |
+         (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)ws) & 15)
+        return FA_ERR_MISALIGNED;
+    if (((uintptr_t)lse | (uintptr_t)cu_seqlens) & 3) return FA_ERR_MISALIGNED;
+    const long long BH = (long long)B * H;
+    const long long cap = ((long long)max_seqlen + kKeysA - 1) / kKeysA * kKeysA;
+    const long long wsh = (long long)kWsRows * ((total + kWsRows - 1) / kWsRows + (long long)B);
+    constexpr int kMaxRpb = 256 / (64 / 8);
+    if (BH > INT_MAX || BH * (cap / kKeysA) > INT_MAX || wsh > INT_MAX ||
+        (cap + kMaxRpb - 1) / kMaxRpb > INT_MAX)
+        return FA_ERR_INVALID_ARG;
+    const size_t tb = (size_t)H * (size_t)total * (size_t)d * 2;
+    const size_t lb = (size_t)H * (size_t)total * 4, cb = ((size_t)B + 1) * 4;
+    const size_t wb = fa_bwd_varlen_workspace_size(B, H, total);
+    const void *ins[7] = {q, k, v, o, dO, lse, cu_seqlens};
+    const size_t insz[7] = {tb, tb, tb, tb, tb, lb, cb};
+    void *outs[4] = {dq, dk, dv, ws};
+    const size_t outsz[4] = {tb, tb, tb, wb};
+    for (int a = 0; a < 4; ++a) {
+        for (int b = 0; b < 7; ++b)
+            if (overlaps(outs[a], outsz[a], ins[b], insz[b])) return FA_ERR_INVALID_ARG;
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(outs[a], outsz[a], outs[b], outsz[b])) return FA_ERR_INVALID_ARG;
+    }
+    const VarlenArgs vl = {cu_seqlens, H, (int)cap, (int)wsh};
+    launch_varlen_fn fn = (dtype == FA_DTYPE_F16) ? pick_varlen<FA_DTYPE_F16>(d, causal)
+                                                  : pick_varlen<FA_DTYPE_BF16>(d, causal);
+    if (fn(q, k, v, o, dO, lse, ws, dq, dk, dv, (int)BH, total, vl, scale, stream) != hipSuccess)
+        return FA_ERR_LAUNCH;
+    return FA_OK;
 }

@@ -289,3 +289,40 @@ def test_varlen_unsupported_and_misaligned():
                  o=4 << 40, lse=5 << 40, cu=6 << 40) == fa.FA_ERR_UNSUPPORTED
     assert vcall(cu=CU + 2) == fa.FA_ERR_MISALIGNED
     assert vcall(v=V + 8) == fa.FA_ERR_MISALIGNED
+
+
+def vbcall(q=Q, k=K, v=V, o=O, do=DO, lse=L, cu=CU, ws=WS, dq=DQ, dk=DK, dv=DV, B=2, H=1,
+           total=64, maxlen=40, d=128, causal=0, scale=0.125, dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_bwd_varlen(q, k, v, o, do, lse, cu, ws, dq, dk, dv, B, H, total, maxlen, d,
+                            causal, scale, dtype, None)
+
+
+def test_varlen_bwd_workspace_size():
+    # per head: 32 * (ceil(total / 32) + B) rows of two fp32 values
+    assert fa.fa_bwd_varlen_workspace_size(1, 1, 1) == 2 * 32 * 2 * 4
+    assert fa.fa_bwd_varlen_workspace_size(3, 2, 100) == 2 * 32 * (4 + 3) * 2 * 4
+    assert fa.fa_bwd_varlen_workspace_size(2, 1, 64) == 32 * (2 + 2) * 2 * 4
+    assert fa.fa_bwd_varlen_workspace_size(0, 1, 64) == 0
+    assert fa.fa_bwd_varlen_workspace_size(1, 0, 64) == 0
+    assert fa.fa_bwd_varlen_workspace_size(1, 1, 0) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(cu=0), dict(ws=0), dict(do=0), dict(dk=0), dict(B=0),
+                                dict(H=0), dict(total=0), dict(maxlen=0), dict(maxlen=65),
+                                dict(causal=2), dict(scale=math.nan), dict(dtype=2),
+                                dict(dq=CU), dict(ws=CU - 16), dict(dv=DQ + 16),
+                                dict(ws=DO), dict(dk=Q + 32)])
+def test_varlen_bwd_invalid(kw):
+    assert vbcall(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_varlen_bwd_unsupported_and_misaligned():
+    assert vbcall(d=80) == fa.FA_ERR_UNSUPPORTED
+    big = dict(total=(1 << 22) + 2, maxlen=(1 << 22) + 1)
+    big.update({n: (i + 1) << 40 for i, n in enumerate(
+        ("q", "k", "v", "o", "do", "lse", "cu", "ws", "dq", "dk", "dv"))})
+    assert vbcall(**big) == fa.FA_ERR_UNSUPPORTED
+    assert vbcall(cu=CU + 2) == fa.FA_ERR_MISALIGNED
+    assert vbcall(ws=WS + 4) == fa.FA_ERR_MISALIGNED
+    assert vbcall(dk=DK + 8) == fa.FA_ERR_MISALIGNED
+    assert vbcall(lse=L + 1) == fa.FA_ERR_MISALIGNED
