@@ -3,8 +3,8 @@
 The calls allocate nothing, never synchronise and only enqueue kernels on
 the stream they are given, so a whole forward + backward step can be
 captured once and replayed.  The test captures fa_fwd, fa_bwd,
-fa_fwd_dropout, fa_bwd_dropout, fa_fwd_split and fa_fwd_window into one
-graph.  It replays the graph three times with new inputs copied into the
+fa_fwd_dropout, fa_bwd_dropout, fa_fwd_split, fa_fwd_window, fa_fwd_varlen
+and fa_bwd_varlen into one graph.  It replays the graph three times with new inputs copied into the
 captured buffers (eager work and synchronisations in between) and checks
 every replay bit for bit against the same calls run eagerly."""
 from __future__ import annotations
@@ -30,7 +30,7 @@ def _ok(st):
 
 
 def test_graph_replay_matches_eager():
-    note("[graph] capture of forward, backward, dropout, split and window calls")
+    note("[graph] capture of forward, backward, dropout, split, window and varlen calls")
     dev = torch.device("cuda", 0)
     B, H, N, d, causal, scale = 1, 3, 700, 128, 1, 0.088
     dt = fa.FA_DTYPE_BF16
@@ -43,7 +43,14 @@ def test_graph_replay_matches_eager():
                             device=dev) for _ in range(2))
     sws = torch.empty(fa.fa_fwd_split_workspace_size(B, H, N, d, 3) // 4, dtype=torch.float32,
                       device=dev)
-    outs = (o, lse, *g1, o2, lse2, *g2, o3, lse3, o4, lse4)
+    # packed layout: q[0] is [H, N, d], three sequences of the N tokens
+    cu = torch.tensor([0, 200, 450, N], dtype=torch.int32, device=dev)
+    o5 = torch.empty_like(q[0])
+    lse5 = torch.empty((H, N), dtype=torch.float32, device=dev)
+    g3 = [torch.empty_like(q[0]) for _ in range(3)]
+    ws3 = torch.empty(fa.fa_bwd_varlen_workspace_size(3, H, N) // 4, dtype=torch.float32,
+                      device=dev)
+    outs = (o, lse, *g1, o2, lse2, *g2, o3, lse3, o4, lse4, o5, lse5, *g3)
 
     def step(stream):
         _ok(fa.fa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, dt, stream))
@@ -54,6 +61,10 @@ def test_graph_replay_matches_eager():
                               77, 5, dt, stream))
         _ok(fa.fa_fwd_split(q, k, v, o3, lse3, B, H, N, d, causal, scale, 3, sws, dt, stream))
         _ok(fa.fa_fwd_window(q, k, v, o4, lse4, B, H, N, d, 200, 0, None, scale, dt, stream))
+        _ok(fa.fa_fwd_varlen(q[0], k[0], v[0], o5, lse5, cu, 3, H, N, 250, d, causal, scale, dt,
+                             stream))
+        _ok(fa.fa_bwd_varlen(q[0], k[0], v[0], o5, do[0], lse5, cu, ws3, *g3, 3, H, N, 250, d,
+                             causal, scale, dt, stream))
 
     def load_inputs(seed):
         a, b, c = make_qkv(B, H, N, d, "bf16", seed=seed)
