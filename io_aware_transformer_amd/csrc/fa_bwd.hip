@@ -536,7 +536,9 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             }
         }
         {
-            constexpr int AH = 2;
+            // one MFMA ahead at d = 128: two ahead overflows the 256 VGPRs
+            // there (K fragments, dK/dV accumulators, S and dP are live)
+            constexpr int AH = D == 128 ? 1 : 2;
             u16x8 a[KT], bv[KT];
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
