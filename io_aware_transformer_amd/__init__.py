@@ -228,6 +228,8 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, stream=
         raise TypeError("q, k, v must share one dtype")
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous [B,H,N,d]")
+    if q.device.type != "cuda" or k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one GPU (there is no CPU path)")
     B, H, N, d = q.shape
     if scale is None:
         scale = d ** -0.5
@@ -253,6 +255,8 @@ def attention_backward(q, k, v, o, lse, do, causal: bool = False, scale: float |
     for t in (k, v, o, do):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
             raise ValueError("k, v, o, do must be contiguous and match q")
+    if any(t.device.type != "cuda" or t.device != q.device for t in (q, k, v, o, lse, do)):
+        raise ValueError("all tensors must be on one GPU (there is no CPU path)")
     B, H, N, d = q.shape
     if scale is None:
         scale = d ** -0.5

@@ -90,3 +90,32 @@ def test_bench_without_gpu_fails_loudly():
     for line in r.stdout.splitlines():
         with pytest.raises(json.JSONDecodeError):
             json.loads(line)
+
+
+def test_binding_has_no_fallback(monkeypatch, tmp_path):
+    """Without the HIP library (and with no way to build it) every entry
+    point raises; nothing computes on the CPU instead."""
+    import io_aware_transformer_amd as fa
+
+    def no_hipcc():
+        raise RuntimeError("hipcc not found: the HIP library cannot be built")
+
+    monkeypatch.setattr(fa, "_lib", None)
+    monkeypatch.setattr(fa, "_LIB_PATH", tmp_path / "missing" / "libfa_fwd.so")
+    monkeypatch.setattr(fa, "_build", no_hipcc)
+    q = torch.zeros((1, 1, 8, 64), dtype=torch.float16)
+    calls = [
+        lambda: fa.fa_fwd(0, 0, 0, 0, 0, 1, 1, 8, 64, 0, 0.125, fa.FA_DTYPE_F16),
+        lambda: fa.fa_bwd(*([0] * 10), 1, 1, 8, 64, 0, 0.125, fa.FA_DTYPE_F16),
+        lambda: fa.fa_fwd_varlen(*([0] * 6), 1, 1, 8, 8, 64, 0, 0.125, fa.FA_DTYPE_F16),
+        lambda: fa.fa_bwd_varlen(*([0] * 11), 1, 1, 8, 8, 64, 0, 0.125, fa.FA_DTYPE_F16),
+        lambda: fa.fa_bwd_workspace_size(1, 1, 8),
+    ]
+    for c in calls:
+        with pytest.raises(RuntimeError, match="hipcc not found"):
+            c()
+    # the tensor-level wrappers refuse CPU tensors outright
+    with pytest.raises(ValueError, match="no CPU path"):
+        fa.attention(q, q, q)
+    with pytest.raises(ValueError, match="no CPU path"):
+        fa.attention_backward(q, q, q, q, torch.zeros((1, 1, 8)), q)
