@@ -441,6 +441,35 @@ def test_bwd_two_key_closed_form(oracle_mod):
     assert dv[0, 0, 1, 0] == pytest.approx(dov[0] * (1 - w[0]) + dov[1] * (1 - w[1]), abs=1e-15)
 
 
+def test_bwd_uniform_weights_closed_form(oracle_mod):
+    """q = 0, causal: P_ij = 1/(i+1), o_i = mean(v_0..v_i), lse_i = ln(i+1),
+    and with the row term from a given o: dV_j = sum_{i>=j} dO_i/(i+1),
+    dK = 0, dQ_i = scale/(i+1) [(sum_{j<=i} k_j v_j^T) dO_i - D_i sum_{j<=i} k_j].
+    The same closed forms check the kernels at the largest sequence length."""
+    N, d, scale = 97, 16, 0.125
+    _, k, v = make_qkv(1, 1, N, d, "f16", seed=6)
+    do = make_qkv(1, 1, N, d, "f16", seed=7)[0]
+    q = torch.zeros_like(k)
+    cnt = np.arange(1, N + 1, dtype=np.float64)
+    v64, k64, do64 = (t[0, 0].double().numpy() for t in (v, k, do))
+    mean = np.cumsum(v64, axis=0) / cnt[:, None]
+    ro, rl = oracle_mod.attn_fwd(bits(q), bits(k), bits(v), "f16", True, scale)
+    np.testing.assert_allclose(ro[0, 0], mean, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(rl[0, 0], np.log(cnt), rtol=0, atol=1e-14)
+    o = torch.from_numpy(mean).to(torch.float16)[None, None]
+    o16 = o[0, 0].double().numpy()
+    dq, dk, dv = oracle_mod.attn_bwd(bits(q), bits(k), bits(v), bits(do), "f16", True, scale,
+                                     o=bits(o))
+    assert not np.any(dk)
+    suffix = np.cumsum((do64 / cnt[:, None])[::-1], axis=0)[::-1]
+    np.testing.assert_allclose(dv[0, 0], suffix, rtol=0, atol=1e-13)
+    kv = np.cumsum(k64[:, :, None] * v64[:, None, :], axis=0)
+    ks = np.cumsum(k64, axis=0)
+    dd = np.sum(do64 * o16, axis=1)
+    want = scale / cnt[:, None] * (np.einsum("iab,ib->ia", kv, do64) - dd[:, None] * ks)
+    np.testing.assert_allclose(dq[0, 0], want, rtol=0, atol=1e-13)
+
+
 # ---------------------------------------------------------------- masks
 
 def test_masked_pin(oracle_mod):
