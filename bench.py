@@ -28,11 +28,14 @@ buffer overwritten before each launch) under "cold".  FLOP =
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import math
 import os
+import re
 import sys
+import threading
 import time
 from pathlib import Path
 
@@ -114,7 +117,57 @@ def time_workload(w, steps: int, warmup: int, seed: int = 0):
         "wall_s": wall,
         "inputs": (q, k, v),
         "outputs": (o, lse),
+        "launch": launch,
     }
+
+
+def read_sclk_mhz(path: str):
+    """The engine clock the driver reports now: the DPM-table line marked '*'
+    of pp_dpm_sclk ('S: 1843Mhz *' on MI355X)."""
+    with open(path) as f:
+        for row in f:
+            if row.rstrip().endswith("*"):
+                m = re.search(r"(\d+)\s*[Mm][Hh]z", row)
+                if m:
+                    return int(m.group(1))
+    return None
+
+
+def observed_sclk(launch, seconds: float = 1.0):
+    """Engine clock sampled every ~10 ms from a host thread while `launch`
+    keeps the GPU busy for about `seconds` (outside the timed region; the
+    clock is power-limited and depends on the load).  None where the driver
+    exposes no pp_dpm_sclk (the first card's is read)."""
+    import torch
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not paths:
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                mhz = read_sclk_mhz(paths[0])
+            except OSError:
+                return
+            if mhz:
+                samples.append(mhz)
+            stop.wait(0.01)
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            launch()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    s = sorted(samples)
+    return {"median": s[len(s) // 2], "min": s[0], "max": s[-1], "samples": len(s),
+            "source": "pp_dpm_sclk"}
 
 
 def time_backward(w, steps: int, warmup: int, seed: int = 0):
@@ -549,6 +602,12 @@ def main() -> int:
             "kernel_us_min": round(res["kernel_ms_min"] * 1e3, 2),
         },
     }
+
+    clk = observed_sclk(res["launch"])
+    line["sclk_mhz"] = clk
+    if clk:
+        log(f"bench: engine clock under the headline load: median {clk['median']} MHz "
+            f"(min {clk['min']}, max {clk['max']}, {clk['samples']} samples)")
 
     if not args.no_cold:
         tc = time_cold(w, min(args.steps, 20))

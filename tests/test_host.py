@@ -119,3 +119,15 @@ def test_binding_has_no_fallback(monkeypatch, tmp_path):
         fa.attention(q, q, q)
     with pytest.raises(ValueError, match="no CPU path"):
         fa.attention_backward(q, q, q, q, torch.zeros((1, 1, 8)), q)
+
+
+def test_bench_reads_the_marked_engine_clock(tmp_path):
+    """bench.py reports the engine clock from the DPM line marked '*'."""
+    import bench
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("S: 1843Mhz *\n0: 500Mhz\n1: 2400Mhz\n")
+    assert bench.read_sclk_mhz(str(f)) == 1843
+    f.write_text("0: 500Mhz\n1: 2400Mhz *\n")
+    assert bench.read_sclk_mhz(str(f)) == 2400
+    f.write_text("0: 500Mhz\n1: 2400Mhz\n")
+    assert bench.read_sclk_mhz(str(f)) is None
