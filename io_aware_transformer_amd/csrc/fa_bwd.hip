@@ -150,8 +150,9 @@ __device__ __forceinline__ u32x4 philox4x32_10(unsigned c0, unsigned c1, unsigne
         }
         const unsigned long long a = (unsigned long long)0xD2511F53u * c0;
         const unsigned long long b = (unsigned long long)0xCD9E8D57u * c2;
-        const unsigned n0 = (unsigned)(b >> 32) ^ c1 ^ k0;
-        const unsigned n2 = (unsigned)(a >> 32) ^ c3 ^ k1;
+        // three-input XORs (v_bitop3 truth table 0x96 = x ^ y ^ z)
+        const unsigned n0 = __builtin_amdgcn_bitop3_b32((unsigned)(b >> 32), c1, k0, 0x96);
+        const unsigned n2 = __builtin_amdgcn_bitop3_b32((unsigned)(a >> 32), c3, k1, 0x96);
         c1 = (unsigned)b;
         c3 = (unsigned)a;
         c0 = n0;
