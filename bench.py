@@ -10,7 +10,7 @@ to stderr.
                   [--workload n8k_causal_peaky] [--secondary n4k_causal]
                   [--backward n8k_causal_peaky] [--window n8k_causal_peaky:1023:0]
                   [--split n4k_h4_causal:4] [--dropout n8k_causal_peaky:0.1]
-                  [--varlen 32:128:8:512:8192]
+                  [--varlen 32:128:8:512:8192] [--spinup 0.3]
                   [--no-cold] [--no-cpu-baseline] [--mode copy]
 
 The headline workload is B=1 H=32 N=8192 d=128 bf16 causal with Q,K x3;
@@ -24,6 +24,11 @@ packed sequences of seeded lengths in [512, 8192] (fa_fwd_varlen, fa_bwd_varlen,
 32 heads) under "varlen", and the headline forward with cold caches (a 512 MB
 buffer overwritten before each launch) under "cold".  FLOP =
 4*B*H*N^2*d, halved when causal (backward: 2.5 times that).
+
+Before the warm-up steps of each record the same call runs back to back,
+untimed, for --spinup seconds (reported as spinup_s): the engine clock goes
+through a transient after idle, and the timed calls should see the clock a
+continuous load settles at.
 """
 from __future__ import annotations
 
@@ -71,6 +76,26 @@ def load_traffic(workload: str):
     return w.get("bytes_per_launch")
 
 
+# Seconds of untimed back-to-back calls before each record's warm-up steps.
+# After idle (process start, or the host preparing the next record's inputs)
+# the engine clock goes through a transient: on MI355X the headline kernel
+# slows from 570 to ~750 us within 3 ms of load and settles at ~550 us only
+# after ~80 ms, longer than ten warm-up calls and the timed calls together.
+SPINUP_S = 0.3
+
+
+def spin(launch, seconds: float | None = None) -> None:
+    """Call launch() back to back, untimed, for about `seconds` of wall time
+    (default SPINUP_S), synchronising every ten calls."""
+    import torch
+    seconds = SPINUP_S if seconds is None else seconds
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            launch()
+        torch.cuda.synchronize()
+
+
 def time_workload(w, steps: int, warmup: int, seed: int = 0):
     import torch
     import io_aware_transformer_amd as fa
@@ -90,6 +115,7 @@ def time_workload(w, steps: int, warmup: int, seed: int = 0):
         if st != fa.FA_OK:
             raise fa.FaError(st)
 
+    spin(launch)
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize(dev)
@@ -197,6 +223,7 @@ def time_backward(w, steps: int, warmup: int, seed: int = 0):
         if st != fa.FA_OK:
             raise fa.FaError(st)
 
+    spin(launch)
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize(dev)
@@ -232,6 +259,7 @@ def time_window(w, window_left: int, window_right: int, steps: int, warmup: int,
         if st != fa.FA_OK:
             raise fa.FaError(st)
 
+    spin(launch)
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize(dev)
@@ -280,6 +308,7 @@ def time_split(w, num_splits: int, steps: int, warmup: int, seed: int = 0):
 
     out = {}
     for name, fn in (("fa_fwd", plain), ("fa_fwd_split", split)):
+        spin(fn)
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize(dev)
@@ -369,6 +398,7 @@ def event_times(launch, stream, steps: int, warmup: int):
     """Per-call times (ms, sorted) of `steps` calls of launch(), each
     bracketed by HIP events on `stream`, after `warmup` untimed calls."""
     import torch
+    spin(launch)
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
@@ -517,6 +547,7 @@ def copy_mode(steps: int) -> None:
 
 
 def main() -> int:
+    global SPINUP_S
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -540,6 +571,10 @@ def main() -> int:
                          "beside ('none' to skip)")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache timing of the headline workload")
+    ap.add_argument("--spinup", type=float, default=SPINUP_S,
+                    help="seconds of untimed back-to-back calls before each record's "
+                         "warm-up steps, so the timed calls see the settled engine clock "
+                         "(0 to skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench")
@@ -553,6 +588,7 @@ def main() -> int:
     if args.mode == "copy":
         copy_mode(args.steps)
         return 0
+    SPINUP_S = max(0.0, args.spinup)
 
     import torch
     import io_aware_transformer_amd as fa
@@ -579,6 +615,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "spinup_s": SPINUP_S,
         "ms_per_step": round(res["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -77,7 +77,8 @@ def test_bench_help_names_every_option():
     r = _bench("--help")
     assert r.returncode == 0
     for opt in ("--gpus", "--steps", "--warmup", "--workload", "--backward", "--window",
-                "--split", "--dropout", "--no-cold", "--no-cpu-baseline"):
+                "--split", "--dropout", "--varlen", "--spinup", "--no-cold",
+                "--no-cpu-baseline"):
         assert opt in r.stdout, opt
 
 
