@@ -108,6 +108,8 @@ def _bind(lib):
                                          p, i64, p, i64, p, p, p]
     lib.oracle_attn_fwd_masked.argtypes = [p, p, p, i32, i64, i64, i64, i64, i64, i64, p,
                                            f64, p, p]
+    lib.oracle_attn_bwd_masked.argtypes = [p, p, p, p, p, i32, i64, i64, i64, i64, i64, i64,
+                                           p, f64, p, p, p]
     u64 = ctypes.c_uint64
     u32 = ctypes.c_uint32
     lib.oracle_philox4x32_10.argtypes = [p, p, p]
@@ -124,6 +126,7 @@ def _bind(lib):
     for name in ("oracle_decode", "oracle_num_threads", "oracle_attn_fwd",
                  "oracle_attn_fwd_rows", "oracle_attn_probs", "oracle_attn_fwd_tiled",
                  "oracle_attn_bwd", "oracle_attn_bwd_rows", "oracle_attn_fwd_masked",
+                 "oracle_attn_bwd_masked",
                  "oracle_dropout_factors", "oracle_attn_fwd_dropout", "oracle_attn_bwd_dropout",
                  "oracle_attn_fwd_dropout_rows", "oracle_attn_bwd_dropout_rows"):
         getattr(lib, name).restype = ctypes.c_int
@@ -321,6 +324,33 @@ def _impl_attn_fwd_masked(lib, q, k, v, dtype, window_left: int, window_right: i
     return o, lse
 
 
+def _impl_attn_bwd_masked(lib, q, k, v, do, dtype, window_left: int, window_right: int,
+                          seqlens, scale: float, o=None):
+    """Gradients of attn_fwd_masked (same window and lengths) for upstream
+    do, in fp64; with o (16-bit bits of a forward output) the row term is
+    dO_i . o_i.  Rows without keys add nothing.  Returns (dq, dk, dv), each
+    [B,H,N,d]."""
+    q, k, v, do = _bits(q), _bits(k), _bits(v), _bits(do)
+    B, H, N, d = _shape(q, k, v)
+    if do.shape != q.shape:
+        raise ValueError("do must have the [B,H,N,d] shape of q")
+    o = _given_o(o, q.shape)
+    sl = None
+    if seqlens is not None:
+        sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+        if sl.shape != (B,):
+            raise ValueError("seqlens must hold one length per batch element")
+    dq = np.empty((B, H, N, d), dtype=np.float64)
+    dk = np.empty_like(dq)
+    dv = np.empty_like(dq)
+    _check(lib.oracle_attn_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(do),
+                                      None if o is None else _ptr(o), _dtype_code(dtype),
+                                      B, H, N, d, int(window_left), int(window_right),
+                                      None if sl is None else _ptr(sl), float(scale),
+                                      _ptr(dq), _ptr(dk), _ptr(dv)), "oracle_attn_bwd_masked")
+    return dq, dk, dv
+
+
 def attn_fwd_varlen(q, k, v, dtype, cu_seqlens, causal: bool, scale: float):
     """Attention over packed variable-length sequences: q, k, v are uint16
     bit patterns [H, total, d]; sequence b holds tokens cu_seqlens[b] ..
@@ -470,8 +500,9 @@ def _impl_attn_bwd_dropout_rows(lib, q, k, v, do, o, dtype, causal: bool, scale:
 
 _API = ("num_threads", "decode", "softmax_1d", "softmax_online_1d", "attn_fwd",
         "attn_fwd_rows", "attn_probs", "attn_fwd_tiled", "attn_bwd", "attn_bwd_rows",
-        "attn_fwd_masked", "philox4x32_10", "dropout_factors", "attn_fwd_dropout",
-        "attn_bwd_dropout", "attn_fwd_dropout_rows", "attn_bwd_dropout_rows")
+        "attn_fwd_masked", "attn_bwd_masked", "philox4x32_10", "dropout_factors",
+        "attn_fwd_dropout", "attn_bwd_dropout", "attn_fwd_dropout_rows",
+        "attn_bwd_dropout_rows")
 
 
 class Oracle:
@@ -511,6 +542,7 @@ attn_fwd_tiled = _module_fn("attn_fwd_tiled")
 attn_bwd = _module_fn("attn_bwd")
 attn_bwd_rows = _module_fn("attn_bwd_rows")
 attn_fwd_masked = _module_fn("attn_fwd_masked")
+attn_bwd_masked = _module_fn("attn_bwd_masked")
 philox4x32_10 = _module_fn("philox4x32_10")
 dropout_factors = _module_fn("dropout_factors")
 attn_fwd_dropout = _module_fn("attn_fwd_dropout")

@@ -707,6 +707,93 @@ int oracle_attn_fwd_masked(const uint16_t *q, const uint16_t *k, const uint16_t 
     return fail ? -2 : 0;
 }
 
+/* Gradients of oracle_attn_fwd_masked for an upstream dO (same mask
+ * reading): per row i with allowed keys lo..hi, P_ij = softmax of the
+ * scores over those keys, dP_ij = dO_i . v_j, D_i = sum_j P_ij dP_ij (or
+ * dO_i . o_i with a given 16-bit o), dS_ij = P_ij (dP_ij - D_i), and
+ *     dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
+ *     dv_j = sum_i P_ij dO_i.
+ * Rows without keys (i >= L_b) add nothing; keys no row may attend get 0.
+ * Heads run in parallel; within a head the rows run in order. */
+int oracle_attn_bwd_masked(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           const uint16_t *dO, const uint16_t *o, int dtype, int64_t B,
+                           int64_t H, int64_t N, int64_t d, int64_t wl, int64_t wr,
+                           const int32_t *seqlens, double scale, double *dq, double *dk,
+                           double *dv)
+{
+    if (seqlens)
+        for (int64_t b = 0; b < B; ++b)
+            if (seqlens[b] < 0 || seqlens[b] > N) return -1;
+    bproblem bp;
+    int rc = load_bproblem(&bp, q, k, v, dO, o, dtype, B, H, N, d, 0, scale);
+    if (rc) return rc;
+    const int64_t n = B * H * N * d;
+    for (int64_t t = 0; t < n; ++t) dq[t] = dk[t] = dv[t] = 0.0;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *pr = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        double *dpr = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        if (!pr || !dpr) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bh = 0; bh < B * H; ++bh) {
+                const int64_t L = seqlens ? seqlens[bh / H] : N;
+                const double *qh = bp.p.q + bh * N * d, *kh = bp.p.k + bh * N * d;
+                const double *vh = bp.p.v + bh * N * d, *doh = bp.dO + bh * N * d;
+                double *dqh = dq + bh * N * d, *dkh = dk + bh * N * d, *dvh = dv + bh * N * d;
+                for (int64_t i = 0; i < L; ++i) {
+                    int64_t lo = wl < 0 ? 0 : i - wl;
+                    int64_t hi = wr < 0 ? L - 1 : i + wr;
+                    if (lo < 0) lo = 0;
+                    if (hi > L - 1) hi = L - 1;
+                    if (lo > hi) continue;
+                    const double *qi = qh + i * d, *doi = doh + i * d;
+                    double m = -INFINITY;
+                    for (int64_t j = lo; j <= hi; ++j) {
+                        double dot = 0.0;
+                        for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
+                        pr[j] = scale * dot;
+                        if (pr[j] > m) m = pr[j];
+                    }
+                    double l = 0.0;
+                    for (int64_t j = lo; j <= hi; ++j) {
+                        pr[j] = exp(pr[j] - m);
+                        l += pr[j];
+                    }
+                    double D = 0.0;
+                    for (int64_t j = lo; j <= hi; ++j) {
+                        pr[j] /= l;
+                        double dp = 0.0;
+                        for (int64_t c = 0; c < d; ++c) dp += doi[c] * vh[j * d + c];
+                        dpr[j] = dp;
+                        D += pr[j] * dp;
+                    }
+                    if (bp.o) {
+                        const double *oi = bp.o + (bh * N + i) * d;
+                        D = 0.0;
+                        for (int64_t c = 0; c < d; ++c) D += doi[c] * oi[c];
+                    }
+                    for (int64_t j = lo; j <= hi; ++j) {
+                        const double ds = pr[j] * (dpr[j] - D);
+                        for (int64_t c = 0; c < d; ++c) {
+                            dqh[i * d + c] += scale * ds * kh[j * d + c];
+                            dkh[j * d + c] += scale * ds * qi[c];
+                            dvh[j * d + c] += pr[j] * doi[c];
+                        }
+                    }
+                }
+            }
+        }
+        free(pr);
+        free(dpr);
+    }
+    free_bproblem(&bp);
+    return fail ? -2 : 0;
+}
+
 /* ---- dropout ---------------------------------------------------------------
  *
  * The pages list dropout among the operations fused into the attention

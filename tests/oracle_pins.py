@@ -345,6 +345,61 @@ def pin_masked(orc) -> bool:
     return ok
 
 
+def masked_grad_reference(q, k, v, do, wl, wr, seqlens, scale):
+    """dQ, dK, dV by torch fp64 autograd through masked_reference's
+    definition: a library softmax over each row's allowed keys (explicit
+    boolean mask), rows without keys giving o = 0."""
+    B, H, N, d = q.shape
+    i = torch.arange(N)[:, None]
+    j = torch.arange(N)[None, :]
+    grads = [np.zeros((B, H, N, d)) for _ in range(3)]
+    for b in range(B):
+        L = N if seqlens is None else int(seqlens[b])
+        allow = (j < L) & (i < L)
+        if wl >= 0:
+            allow &= j >= i - wl
+        if wr >= 0:
+            allow &= j <= i + wr
+        has = allow.any(-1)
+        if not bool(has.any()):
+            continue
+        qq, kk, vv = (t[b].double().clone().requires_grad_() for t in (q, k, v))
+        s = torch.matmul(qq, kk.transpose(-1, -2)) * float(scale)
+        s = s.masked_fill(~allow, float("-inf"))
+        o = torch.matmul(torch.softmax(s[:, has], dim=-1), vv)
+        (o * do[b].double()[:, has]).sum().backward()
+        for g, t in zip(grads, (qq, kk, vv)):
+            g[b] = t.grad.numpy()
+    return tuple(grads)
+
+
+def pin_bwd_masked(orc) -> bool:
+    ok = True
+    q, k, v = _qkv(3, 2, 21, 8, "bf16", seed=30)
+    do = _qkv(3, 2, 21, 8, "bf16", seed=31)[0]
+    # no window, no padding = the plain gradients; (-1, 0) = causal; also
+    # with the row term from a given o
+    o16 = _qkv(3, 2, 21, 8, "bf16", seed=32)[0]
+    for causal, (wl, wr) in ((False, (-1, -1)), (True, (-1, 0))):
+        for given in (None, bits(o16)):
+            g = orc.attn_bwd_masked(bits(q), bits(k), bits(v), bits(do), "bf16", wl, wr, None,
+                                    0.35, o=given)
+            r = orc.attn_bwd(bits(q), bits(k), bits(v), bits(do), "bf16", causal, 0.35,
+                             o=given)
+            ok &= all(_close(a, c, 1e-14) for a, c in zip(g, r))
+    # windows and lengths against autograd through a library softmax
+    for (wl, wr), lens in (((4, 0), None), ((3, 2), [21, 15, 0]), ((0, 0), None),
+                           ((-1, 5), [5, 21, 1]), ((6, -1), [20, 2, 21])):
+        g = orc.attn_bwd_masked(bits(q), bits(k), bits(v), bits(do), "bf16", wl, wr, lens, 0.35)
+        r = masked_grad_reference(q, k, v, do, wl, wr, lens, 0.35)
+        ok &= all(_close(a, c, 1e-12) for a, c in zip(g, r))
+        # padded rows and keys get no gradient
+        if lens is not None:
+            for b, L in enumerate(lens):
+                ok &= all(bool(np.all(x[b, :, L:] == 0.0)) for x in g)
+    return ok
+
+
 # ---------------------------------------------------------------- dropout
 
 def pin_philox_kat(orc) -> bool:
@@ -460,6 +515,7 @@ PINS = {
     "bwd_rows": pin_bwd_rows,
     "bwd_given_o": pin_bwd_given_o,
     "masked": pin_masked,
+    "bwd_masked": pin_bwd_masked,
     "philox_kat": pin_philox_kat,
     "dropout": pin_dropout,
     "dropout_rows": pin_dropout_rows,

@@ -297,6 +297,16 @@ _ROWS_LOOP = ("\n                    const double *qi = bp.p.q + (bh * N + i) * 
               "\n                    const double ds = pij * (dp")
 
 MUTANTS = [
+    ("const double ds = pr[j] * (dpr[j] - D);", "const double ds = pr[j] * dpr[j];",
+     "masked bwd: row term D dropped"),
+    ("dvh[j * d + c] += pr[j] * doi[c];", "dvh[j * d + c] += pr[j] * qi[c];",
+     "masked bwd: dV from q instead of dO"),
+    ("for (int64_t i = 0; i < L; ++i) {\n                    int64_t lo",
+     "for (int64_t i = 0; i < N; ++i) {\n                    int64_t lo",
+     "masked bwd: rows past the valid length attend"),
+    ("dkh[j * d + c] += scale * ds * qi[c];\n                            dvh[j * d + c] += pr[j]",
+     "dkh[j * d + c] -= scale * ds * qi[c];\n                            dvh[j * d + c] += pr[j]",
+     "masked bwd: dK sign"),
     ("s[j] = p->scale * dot;\n        if (s[j] > m) m = s[j];\n    }\n    /* pass 2",
      "s[j] = dot;\n        if (s[j] > m) m = s[j];\n    }\n    /* pass 2", "dropped scale"),
     ("        double w = exp(s[j] - m);", "        double w = exp(m - s[j]);", "sign of the exponent"),
@@ -351,7 +361,11 @@ MUTANTS = [
     ("const int64_t nkeys = p->causal ? i + 1 : N;\n    double m = -INFINITY;\n    for (int64_t j = 0; j < nkeys; ++j) {\n        double dot = 0.0;\n        for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];\n        prow[j]",
      "const int64_t nkeys = p->causal ? N : N;\n    double m = -INFINITY;\n    for (int64_t j = 0; j < nkeys; ++j) {\n        double dot = 0.0;\n        for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];\n        prow[j]",
      "bwd: causal mask dropped in the row weights"),
-    ("dp += doi[c] * vh[j * d + c];", "dp += doi[c] * vh[i * d + c];", "bwd: dP row index of V"),
+    ("dp += doi[c] * vh[j * d + c];\n        dprow[j] = dp;",
+     "dp += doi[c] * vh[i * d + c];\n        dprow[j] = dp;", "bwd: dP row index of V"),
+    ("dp += doi[c] * vh[j * d + c];\n                        dpr[j] = dp;",
+     "dp += doi[c] * vh[i * d + c];\n                        dpr[j] = dp;",
+     "masked bwd: dP row index of V"),
     ("const double ds = pij * (dp - Dall[bh * N + i]);",
      "const double ds = pij * (Dall[bh * N + i] - dp);", "bwd rows: sign of dS"),
     ("for (int64_t i = causal ? j : 0; i < N; ++i) {" + _ROWS_LOOP,
@@ -363,16 +377,27 @@ MUTANTS = [
     ("(dprow[j] - D);\n                    for (int64_t c = 0; c < d; ++c) out[c] += scale * ds",
      "(dprow[j] - D);\n                    for (int64_t c = 0; c < d; ++c) out[c] += ds",
      "bwd rows: dQ without scale"),
-    ("for (int64_t c = 0; c < d; ++c) D += doi[c] * oi[c];",
-     "for (int64_t c = 0; c < d; ++c) D += doi[c] * oi[0];", "bwd: given-o row term index"),
-    ("int64_t lo = wl < 0 ? 0 : i - wl;", "int64_t lo = wl < 0 ? 0 : i - wl + 1;",
+    ("        D = 0.0;\n        for (int64_t c = 0; c < d; ++c) D += doi[c] * oi[c];",
+     "        D = 0.0;\n        for (int64_t c = 0; c < d; ++c) D += doi[c] * oi[0];",
+     "bwd: given-o row term index"),
+    ("D = 0.0;\n                        for (int64_t c = 0; c < d; ++c) D += doi[c] * oi[c];",
+     "D = 0.0;\n                        for (int64_t c = 0; c < d; ++c) D += doi[c] * oi[0];",
+     "masked bwd: given-o row term index"),
+    ("\n                int64_t lo = wl < 0 ? 0 : i - wl;", "\n                int64_t lo = wl < 0 ? 0 : i - wl + 1;",
      "mask: window left edge off by one"),
+    ("\n                    int64_t lo = wl < 0 ? 0 : i - wl;", "\n                    int64_t lo = wl < 0 ? 0 : i - wl + 1;",
+     "masked bwd: window left edge off by one"),
     ("const int64_t L = seqlens ? seqlens[b] : N;",
      "const int64_t L = seqlens ? seqlens[b] + (seqlens[b] < N) : N;",
      "mask: padding keeps key L"),
-    ("int64_t hi = wr < 0 ? L - 1 : i + wr;", "int64_t hi = wr < 0 ? L - 1 : i + wr + 1;",
+    ("\n                int64_t hi = wr < 0 ? L - 1 : i + wr;", "\n                int64_t hi = wr < 0 ? L - 1 : i + wr + 1;",
      "mask: window right edge off by one"),
-    ("if (hi > L - 1) hi = L - 1;", "if (hi > N - 1) hi = N - 1;", "mask: window ignores padding"),
+    ("\n                    int64_t hi = wr < 0 ? L - 1 : i + wr;", "\n                    int64_t hi = wr < 0 ? L - 1 : i + wr + 1;",
+     "masked bwd: window right edge off by one"),
+    ("\n                if (hi > L - 1) hi = L - 1;", "\n                if (hi > N - 1) hi = N - 1;",
+     "mask: window ignores padding"),
+    ("\n                    if (hi > L - 1) hi = L - 1;", "\n                    if (hi > N - 1) hi = N - 1;",
+     "masked bwd: window ignores padding"),
     ("if (i >= L || lo > hi) {", "if (lo > hi) {", "mask: padded rows not emptied"),
     ("            k0 += 0x9E3779B9u;", "            k0 += 0x9E3779B7u;", "philox: key bump constant"),
     ("        c0 = hi1 ^ c1 ^ k0;", "        c0 = hi0 ^ c1 ^ k0;", "philox: round word order"),
@@ -474,6 +499,10 @@ def test_bwd_uniform_weights_closed_form(oracle_mod):
 
 def test_masked_pin(oracle_mod):
     assert PINS["masked"](oracle_mod)
+
+
+def test_bwd_masked_pin(oracle_mod):
+    assert PINS["bwd_masked"](oracle_mod)
 
 
 @pytest.mark.parametrize("wl,wr", [(-1, -1), (-1, 0), (0, 0), (7, 0), (7, 3), (-1, 4), (40, 40)])
