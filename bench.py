@@ -16,8 +16,8 @@ to stderr.
 The headline workload is B=1 H=32 N=8192 d=128 bf16 causal with Q,K x3;
 B=2 H=16 N=4096 d=128 bf16 causal is reported beside it, and the backward
 pass (fa_bwd) of the headline workload under "backward", and a sliding-window
-forward (fa_fwd_window, each query sees the 1024 keys ending at itself) under
-"window", and fa_fwd against fa_fwd_split on a few-head shape under "split", and
+forward and backward (fa_fwd_window, fa_bwd_window; each query sees the 1024 keys
+ending at itself) under "window", and fa_fwd against fa_fwd_split on a few-head shape under "split", and
 the dropout forward and backward (fa_fwd_dropout, fa_bwd_dropout, p = 0.1) of the
 headline workload under "dropout", a causal bf16 forward and backward over 8
 packed sequences of seeded lengths in [512, 8192] (fa_fwd_varlen, fa_bwd_varlen,
@@ -275,8 +275,23 @@ def time_window(w, window_left: int, window_right: int, steps: int, warmup: int,
     lo = torch.clamp(i - window_left, min=0) if window_left >= 0 else torch.zeros_like(i)
     hi = torch.clamp(i + window_right, max=w.N - 1) if window_right >= 0 else torch.full_like(i, w.N - 1)
     pairs = float((hi - lo + 1).sum()) * w.B * w.H
+
+    # fa_bwd_window on this forward's o and lse and a seeded dO
+    from io_aware_transformer_amd.inputs import make_qkv
+    do = make_qkv(w.B, w.H, w.N, w.d, w.dtype, seed=seed + 12345)[0].to(dev)
+    ws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.H, w.N) // 4, dtype=torch.float32,
+                     device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+
+    def backward():
+        st = fa.fa_bwd_window(q, k, v, o, do, lse, ws, dq, dk, dv, w.B, w.H, w.N, w.d,
+                              window_left, window_right, None, w.scale, dt, stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    per_b = event_times(backward, stream, steps, warmup)
     return {"ms_mean": sum(per) / len(per), "ms_median": per[len(per) // 2],
-            "flop": 4.0 * w.d * pairs}
+            "flop": 4.0 * w.d * pairs, "bwd_ms_mean": sum(per_b) / len(per_b)}
 
 
 def time_split(w, num_splits: int, steps: int, warmup: int, seed: int = 0):
@@ -695,11 +710,16 @@ def main() -> int:
         ww = WORKLOADS[wname]
         rw = time_window(ww, int(wl), int(wr), args.steps, args.warmup)
         tw = rw["flop"] / (rw["ms_mean"] * 1e-3) / 1e12
+        twb = 2.5 * rw["flop"] / (rw["bwd_ms_mean"] * 1e-3) / 1e12
         log(f"bench: window ({wl},{wr}) on {ww.name} mean {rw['ms_mean']*1e3:.1f} us, "
-            f"{tw:.1f} TFLOP/s of allowed pairs")
+            f"{tw:.1f} TFLOP/s of allowed pairs; backward {rw['bwd_ms_mean']*1e3:.1f} us, "
+            f"{twb:.1f} TFLOP/s")
         line["window"] = {"workload": ww.name, "window_left": int(wl), "window_right": int(wr),
                           "flop_per_step": rw["flop"], "ms_mean": round(rw["ms_mean"], 5),
-                          "tflops": round(tw, 2), "frac": round(tw / PEAK_BF16_TFLOPS, 4)}
+                          "tflops": round(tw, 2), "frac": round(tw / PEAK_BF16_TFLOPS, 4),
+                          "bwd_ms_mean": round(rw["bwd_ms_mean"], 5),
+                          "bwd_tflops": round(twb, 2),
+                          "bwd_frac": round(twb / PEAK_BF16_TFLOPS, 4)}
 
     if args.split and args.split != "none":
         sname, ns = args.split.split(":")

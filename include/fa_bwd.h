@@ -82,6 +82,27 @@ fa_status fa_bwd_dropout(const void *q, const void *k, const void *v, const void
                          float p_drop, unsigned long long seed, unsigned offset,
                          fa_dtype dtype, hipStream_t stream);
 
+/* Backward pass of fa_fwd_window: the gradients fa_bwd computes, over the
+ * allowed (query, key) pairs of fa_fwd_window's mask,
+ *     max(0, i - window_left) <= j <= min(L_b - 1, i + window_right),
+ * the sliding-window and padding masks of "FlashAttention 优化原理与实现要点解析"
+ * §8 (reading as in fa_fwd.h).  Rows i >= L_b, which attend nothing, and
+ * keys j >= L_b, which nothing attends, get zero gradients.
+ *   o, lse          as fa_fwd_window wrote them for the same q, k, v, window,
+ *                   seqlens and scale (rows i >= L_b: o = 0, lse = -inf)
+ *   window_left, window_right, seqlens: as fa_fwd_window (sides >= -1, -1 =
+ *                   open; seqlens device int32 [B] clamped to 0..N, or NULL)
+ *   ws              fa_bwd_workspace_size(B, H, N) bytes, 16-byte aligned
+ * Other arguments, layouts and errors as fa_bwd; FA_ERR_INVALID_ARG also for
+ * a window side below -1 or seqlens overlapping an output, FA_ERR_MISALIGNED
+ * for seqlens not 4-byte aligned.  seqlens is only read.  (-1, -1) without
+ * seqlens gives fa_bwd's non-causal result and (-1, 0) its causal one. */
+fa_status fa_bwd_window(const void *q, const void *k, const void *v, const void *o,
+                        const void *dO, const float *lse, float *ws, void *dq, void *dk,
+                        void *dv, int B, int H, int N, int d, int window_left,
+                        int window_right, const int *seqlens, float scale, fa_dtype dtype,
+                        hipStream_t stream);
+
 /* Bytes of fp32 workspace fa_bwd_varlen needs (0 if a size is not
  * positive): per head, 32 * (ceil(total / 32) + B) rows of (lse, D). */
 size_t fa_bwd_varlen_workspace_size(int B, int H, int total);

@@ -24,6 +24,8 @@ C entry points mirrored here with the same names and argument order:
                  dtype, stream) -> status
   fa_bwd_dropout(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale,
                  p_drop, seed, offset, dtype, stream) -> status
+  fa_bwd_window(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, window_left,
+                window_right, seqlens, scale, dtype, stream) -> status
   fa_bwd_varlen(q, k, v, o, dO, lse, cu_seqlens, ws, dq, dk, dv, B, H, total,
                 max_seqlen, d, causal, scale, dtype, stream) -> status
   fa_bwd_varlen_workspace_size(B, H, total) -> bytes
@@ -49,7 +51,7 @@ FA_DTYPE_BF16 = 1
 EXPORTED = ("fa_fwd_f16", "fa_fwd_bf16", "fa_fwd", "fa_fwd_window", "fa_fwd_split",
             "fa_fwd_split_workspace_size", "fa_status_string", "fa_bwd",
             "fa_bwd_workspace_size", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_varlen",
-            "fa_bwd_varlen", "fa_bwd_varlen_workspace_size")
+            "fa_bwd_varlen", "fa_bwd_varlen_workspace_size", "fa_bwd_window")
 FA_MAX_SPLITS = 64
 
 _lib = None
@@ -102,6 +104,8 @@ def load():
     lib.fa_fwd_dropout.restype = ctypes.c_int
     lib.fa_bwd_dropout.argtypes = [p] * 10 + [i, i, i, i, i, f, f, u64, u32, i, p]
     lib.fa_bwd_dropout.restype = ctypes.c_int
+    lib.fa_bwd_window.argtypes = [p] * 10 + [i, i, i, i, i, i, p, f, i, p]
+    lib.fa_bwd_window.restype = ctypes.c_int
     lib.fa_bwd_varlen.argtypes = [p] * 11 + [i, i, i, i, i, i, f, i, p]
     lib.fa_bwd_varlen.restype = ctypes.c_int
     lib.fa_bwd_varlen_workspace_size.argtypes = [i, i, i]
@@ -193,6 +197,14 @@ def fa_bwd_dropout(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scal
                                  _ptr(ws), _ptr(dq), _ptr(dk), _ptr(dv), int(B), int(H),
                                  int(N), int(d), int(causal), float(scale), float(p_drop),
                                  int(seed), int(offset), int(dtype), _stream(stream))
+
+
+def fa_bwd_window(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, window_left, window_right,
+                  seqlens, scale, dtype, stream=None) -> int:
+    return load().fa_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+                                _ptr(ws), _ptr(dq), _ptr(dk), _ptr(dv), int(B), int(H), int(N),
+                                int(d), int(window_left), int(window_right), _ptr(seqlens),
+                                float(scale), int(dtype), _stream(stream))
 
 
 def fa_bwd_varlen(q, k, v, o, dO, lse, cu_seqlens, ws, dq, dk, dv, B, H, total, max_seqlen, d,

@@ -197,6 +197,22 @@ __device__ __forceinline__ Seq varlen_seq(const VarlenArgs &vl, int bh, int tota
     return s;
 }
 
+// Sliding window and valid lengths (WIN kernels): query i of batch element
+// b may attend key j when (wl < 0 or j >= i - wl) and (wr < 0 or j <= i + wr)
+// and both i and j are below the element's valid length L_b.
+struct WindowArgs {
+    const int *lens;   // device int32 [B] valid lengths (clamped to 0..N), or null
+    int H, wl, wr;
+};
+__device__ __forceinline__ int window_len(const WindowArgs &wa, int bh, int N)
+{
+    return wa.lens ? min(max(wa.lens[bh / wa.H], 0), N) : N;
+}
+__device__ __forceinline__ bool window_allows(const WindowArgs &wa, int lb, int i, int j)
+{
+    return i < lb && j < lb && (wa.wl < 0 || j >= i - wa.wl) && (wa.wr < 0 || j <= i + wa.wr);
+}
+
 // Byte transpose of a 4x4 byte matrix held by the 4 lanes of a quad (lane e
 // holds row e as one word): afterwards lane e holds column e.  Two stages:
 // swap 16-bit halves with lane e^2, then bytes with lane e^1 (DPP quad
@@ -314,15 +330,16 @@ void fa_bwd_delta_varlen_kernel(const u16 *__restrict__ O, const u16 *__restrict
 // (query qs + l32, key half hh) of each step and the 32 x 32 bytes are
 // transposed through a per-wave LDS block: a byte transpose inside each
 // lane quad, 4 dword writes, and in the step one 16-byte read per lane.
-template <int DT, int D, bool CAUSAL, bool DROP, bool VARLEN>
+template <int DT, int D, bool CAUSAL, bool DROP, bool VARLEN, bool WIN = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                         const u16 *__restrict__ V, const u16 *__restrict__ dO,
                         const float *__restrict__ WS, u16 *__restrict__ dK,
                         u16 *__restrict__ dV, int BH, int N_in, int nblk_in, float c2,
-                        float scale, DropArgs dr, VarlenArgs vl)
+                        float scale, DropArgs dr, VarlenArgs vl, WindowArgs wa)
 {
     static_assert(!(DROP && VARLEN), "dropout is built for the batched layout");
+    static_assert(!(WIN && (CAUSAL || DROP || VARLEN)), "the window kernels stand alone");
     using E = Elem<DT>;
     using T = Tile<D>;
     constexpr int KT = D / 16;                 // MFMA k-steps over d
@@ -405,7 +422,25 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     }
 
     const int n_qt = (N + kQT - 1) / kQT;
-    const int t0 = CAUSAL ? k0 / kQT : 0;
+    int t0 = CAUSAL ? k0 / kQT : 0, t_end = n_qt;
+    // window: the query rows any key of this work-group may be attended by,
+    // and this wave's (rows past lb and keys past lb take no part)
+    int lb = N, wq_lo = 0, wq_hi = -1;
+    if constexpr (WIN) {
+        lb = window_len(wa, bh, N);
+        const int k_last = min(k0 + kKeysA, lb) - 1;
+        const int q_lo = wa.wr < 0 ? 0 : max(0, k0 - wa.wr);
+        const int q_hi = wa.wl < 0 ? lb - 1 : min(lb - 1, k_last + wa.wl);
+        t0 = t_end = 0;
+        if (k0 < lb && q_lo <= q_hi) {
+            t0 = q_lo / kQT;
+            t_end = q_hi / kQT + 1;
+        }
+        if (kw < lb) {
+            wq_lo = wa.wr < 0 ? 0 : kw - wa.wr;
+            wq_hi = wa.wl < 0 ? lb - 1 : min(lb - 1, min(kw + 31, lb - 1) + wa.wl);
+        }
+    }
     const int ws_wave = __builtin_amdgcn_readfirstlane(w);
 
     auto issue = [&](auto par, int t) {
@@ -498,7 +533,7 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     // MFMA loop reads its LDS operands a fixed distance ahead, and the
     // interleave is pinned (scheduling-group barriers) so that neither the
     // reads crowd the registers nor each MFMA waits on its own read.
-    auto step = [&](auto par, int u, bool diag) {
+    auto step = [&](auto par, int u, bool diag, int qs) {
         LDS unsigned char *qb = qbuf(par);
         LDS unsigned char *ob = obuf(par);
         LDS float *wb = wbuf(par) + u * 2 * kWsRows;
@@ -577,7 +612,12 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float x = fmaf(s[4 * g + e], c2, -l4[e]);
-                if (diag && l32 > 8 * g + 4 * hh + e) x = neg_inf();
+                if constexpr (WIN) {
+                    if (diag && !window_allows(wa, lb, qs + 8 * g + 4 * hh + e, kw + l32))
+                        x = neg_inf();
+                } else if (diag && l32 > 8 * g + 4 * hh + e) {
+                    x = neg_inf();
+                }
                 p[e] = __builtin_amdgcn_exp2f(x);
                 if constexpr (DROP) {
                     // dS = P (Z dP - D), and P Z for the dV product
@@ -626,7 +666,7 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
     auto tile = [&](auto par, int t) {
         constexpr int P = decltype(par)::value;
-        if (t + 1 < n_qt) issue(Buf<1 - P>{}, t + 1);
+        if (t + 1 < t_end) issue(Buf<1 - P>{}, t + 1);
         if constexpr (DROP) drop_tile(t);
 #pragma unroll
         for (int u = 0; u < kQT / 32; ++u) {
@@ -634,20 +674,29 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             // under dropout a step wholly past N (which adds nothing) is
             // skipped too: the branch keeps the register allocator from
             // spilling across the fused steps of the non-causal kernel
-            if ((!CAUSAL || qs + 31 >= kw) && (!DROP || qs < N))
-                step(par, u, CAUSAL && qs == kw);
+            if constexpr (WIN) {
+                // some pair of the step allowed; a mask unless all are
+                if (qs <= wq_hi && qs + 31 >= wq_lo) {
+                    const bool all = (wa.wr < 0 || kw + 31 <= qs + wa.wr) &&
+                                     (wa.wl < 0 || kw >= qs + 31 - wa.wl) &&
+                                     kw + 31 < lb && qs + 31 < lb;
+                    step(par, u, !all, qs);
+                }
+            } else if ((!CAUSAL || qs + 31 >= kw) && (!DROP || qs < N)) {
+                step(par, u, CAUSAL && qs == kw, qs);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
 
-    if (t0 < n_qt) issue(Buf<0>{}, t0);
+    if (t0 < t_end) issue(Buf<0>{}, t0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int t = t0; t < n_qt; t += 2) {
+    for (int t = t0; t < t_end; t += 2) {
         tile(Buf<0>{}, t);
-        if (t + 1 < n_qt) tile(Buf<1>{}, t + 1);
+        if (t + 1 < t_end) tile(Buf<1>{}, t + 1);
     }
 
     // epilogue: dK = scale dK^T, dV = dV^T, rows of key `key`, d = 32db + 8g + 4hh + e
@@ -673,14 +722,16 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
 // DROP: dS = P o (Z o dP - D) with the forward's keep factors Z; a lane
 // holds 16 keys of one query, the 16 bytes of one Philox call per step.
-template <int DT, int D, bool CAUSAL, bool DROP, bool VARLEN>
+template <int DT, int D, bool CAUSAL, bool DROP, bool VARLEN, bool WIN = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                       const u16 *__restrict__ V, const u16 *__restrict__ dO,
                       const float *__restrict__ WS, u16 *__restrict__ dQ, int BH, int N_in,
-                      int nblk, int nqb, float c2, float scale, DropArgs dr, VarlenArgs vl)
+                      int nblk, int nqb, float c2, float scale, DropArgs dr, VarlenArgs vl,
+                      WindowArgs wa)
 {
     static_assert(!(DROP && VARLEN), "dropout is built for the batched layout");
+    static_assert(!(WIN && (CAUSAL || DROP || VARLEN)), "the window kernels stand alone");
     using E = Elem<DT>;
     using T = Tile<D>;
     constexpr int KT = D / 16;
@@ -748,8 +799,27 @@ void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
     const int n_kt32 = (N + 31) / 32;
     const int n_steps = CAUSAL ? min(n_kt32, (qblk + 1) * (kQB / 32)) : n_kt32;
-    const int n_tiles = (n_steps + 1) / 2;
+    int t_begin = 0, t_end = (n_steps + 1) / 2;
     const int n_w = (q0 >= N) ? 0 : (CAUSAL ? min(n_steps, q0 / 32 + 1) : n_steps);
+    // window: the keys any row of this work-group may attend, and this
+    // wave's (rows past lb and keys past lb take no part)
+    int lb = N, wk_lo = 0, wk_hi = -1;
+    if constexpr (WIN) {
+        lb = window_len(wa, bh, N);
+        const int qb0 = qblk * kQB;
+        const int q_last = min(qb0 + kQB, lb) - 1;
+        const int k_lo = wa.wl < 0 ? 0 : max(0, qb0 - wa.wl);
+        const int k_hi = wa.wr < 0 ? lb - 1 : min(lb - 1, q_last + wa.wr);
+        t_begin = t_end = 0;
+        if (qb0 < lb && k_lo <= k_hi) {
+            t_begin = k_lo / kKT;
+            t_end = k_hi / kKT + 1;
+        }
+        if (q0 < lb) {
+            wk_lo = wa.wl < 0 ? 0 : q0 - wa.wl;
+            wk_hi = wa.wr < 0 ? lb - 1 : min(lb - 1, min(q0 + 31, lb - 1) + wa.wr);
+        }
+    }
 
     auto issue = [&](auto par, int t) {
 #pragma unroll
@@ -841,7 +911,12 @@ void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float x = fmaf(s[4 * g + e], c2, -l2);
-                if (diag && ks0 + 8 * g + 4 * hh + e > qrow) x = neg_inf();
+                if constexpr (WIN) {
+                    if (diag && !window_allows(wa, lb, qrow, ks0 + 8 * g + 4 * hh + e))
+                        x = neg_inf();
+                } else if (diag && ks0 + 8 * g + 4 * hh + e > qrow) {
+                    x = neg_inf();
+                }
                 if constexpr (DROP) {
                     const float zf = ((zb[g] >> (8 * e)) & 0xffu) < dr.thr ? dr.fscale : 0.f;
                     ds[e] = __builtin_amdgcn_exp2f(x) * fmaf(zf, dp[4 * g + e], -dd);
@@ -877,23 +952,33 @@ void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
     auto tile = [&](auto par, int t) {
         constexpr int P = decltype(par)::value;
-        if (t + 1 < n_tiles) issue(Buf<1 - P>{}, t + 1);
+        if (t + 1 < t_end) issue(Buf<1 - P>{}, t + 1);
 #pragma unroll
         for (int u = 0; u < kKT / 32; ++u) {
             const int j = t * (kKT / 32) + u;  // 32-key step index
-            if (j < n_w) step(par, u, CAUSAL && 32 * j + 31 > q0, 32 * j);
+            if constexpr (WIN) {
+                const int ks = 32 * j;
+                if (ks <= wk_hi && ks + 31 >= wk_lo) {
+                    const bool all = (wa.wl < 0 || ks >= q0 + 31 - wa.wl) &&
+                                     (wa.wr < 0 || ks + 31 <= q0 + wa.wr) &&
+                                     ks + 31 < lb && q0 + 31 < lb;
+                    step(par, u, !all, ks);
+                }
+            } else if (j < n_w) {
+                step(par, u, CAUSAL && 32 * j + 31 > q0, 32 * j);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
 
-    if (n_tiles > 0) issue(Buf<0>{}, 0);
+    if (t_begin < t_end) issue(Buf<0>{}, t_begin);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int t = 0; t < n_tiles; t += 2) {
+    for (int t = t_begin; t < t_end; t += 2) {
         tile(Buf<0>{}, t);
-        if (t + 1 < n_tiles) tile(Buf<1>{}, t + 1);
+        if (t + 1 < t_end) tile(Buf<1>{}, t + 1);
     }
 
     if (qrow < N) {
@@ -924,6 +1009,7 @@ hipError_t launch(const void *q, const void *k, const void *v, const void *o, co
                   float scale, DropArgs dr, hipStream_t stream)
 {
     const VarlenArgs vl = {nullptr, 1, 0, 0};
+    const WindowArgs wa = {nullptr, 1, -1, -1};
     const int nblk = (N + kWsRows - 1) / kWsRows;
     const long long rows_padded = (long long)BH * nblk * kWsRows;
     constexpr int RPB = 256 / (D / 8);
@@ -936,11 +1022,11 @@ hipError_t launch(const void *q, const void *k, const void *v, const void *o, co
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D, CAUSAL, DROP, false>),
                        dim3((unsigned)((long long)BH * nkb)), dim3(kThreads), 0, stream,
                        (const u16 *)q, (const u16 *)k, (const u16 *)v, (const u16 *)dO,
-                       (const float *)ws, (u16 *)dk, (u16 *)dv, BH, N, nblk, c2, scale, dr, vl);
+                       (const float *)ws, (u16 *)dk, (u16 *)dv, BH, N, nblk, c2, scale, dr, vl, wa);
     hipLaunchKernelGGL((fa_bwd_dq_kernel<DT, D, CAUSAL, DROP, false>),
                        dim3((unsigned)((long long)BH * nqb)), dim3(kThreads), 0, stream,
                        (const u16 *)q, (const u16 *)k, (const u16 *)v, (const u16 *)dO,
-                       (const float *)ws, (u16 *)dq, BH, N, nblk, nqb, c2, scale, dr, vl);
+                       (const float *)ws, (u16 *)dq, BH, N, nblk, nqb, c2, scale, dr, vl, wa);
     return hipGetLastError();
 }
 
@@ -954,6 +1040,7 @@ hipError_t launch_varlen(const void *q, const void *k, const void *v, const void
 {
     constexpr int RPB = 256 / (D / 8);
     const DropArgs dr = {0u, 0u, 0u, 256u, 1.f};
+    const WindowArgs wa = {nullptr, 1, -1, -1};
     const float c2 = scale * kLog2e;
     const int nb = vl.cap / kKeysA;            // key blocks = Q blocks per sequence
     hipLaunchKernelGGL((fa_bwd_delta_varlen_kernel<DT, D>),
@@ -962,11 +1049,11 @@ hipError_t launch_varlen(const void *q, const void *k, const void *v, const void
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D, CAUSAL, false, true>),
                        dim3((unsigned)((long long)BH * nb)), dim3(kThreads), 0, stream,
                        (const u16 *)q, (const u16 *)k, (const u16 *)v, (const u16 *)dO,
-                       (const float *)ws, (u16 *)dk, (u16 *)dv, BH, total, 0, c2, scale, dr, vl);
+                       (const float *)ws, (u16 *)dk, (u16 *)dv, BH, total, 0, c2, scale, dr, vl, wa);
     hipLaunchKernelGGL((fa_bwd_dq_kernel<DT, D, CAUSAL, false, true>),
                        dim3((unsigned)((long long)BH * nb)), dim3(kThreads), 0, stream,
                        (const u16 *)q, (const u16 *)k, (const u16 *)v, (const u16 *)dO,
-                       (const float *)ws, (u16 *)dq, BH, total, 0, nb, c2, scale, dr, vl);
+                       (const float *)ws, (u16 *)dq, BH, total, 0, nb, c2, scale, dr, vl, wa);
     return hipGetLastError();
 }
 
@@ -979,6 +1066,36 @@ launch_varlen_fn pick_varlen(int d, int causal)
 {
     if (d == 64) return causal ? launch_varlen<DT, 64, true> : launch_varlen<DT, 64, false>;
     return causal ? launch_varlen<DT, 128, true> : launch_varlen<DT, 128, false>;
+}
+
+// Window and valid lengths: the batched row-term kernel, then the WIN walking
+// kernels over the full [B,H,N,d] grid.
+template <int DT, int D>
+hipError_t launch_window(const void *q, const void *k, const void *v, const void *o,
+                         const void *dO, const float *lse, float *ws, void *dq, void *dk,
+                         void *dv, int BH, int N, WindowArgs wa, float scale, hipStream_t stream)
+{
+    const VarlenArgs vl = {nullptr, 1, 0, 0};
+    const DropArgs dr = {0u, 0u, 0u, 256u, 1.f};
+    const int nblk = (N + kWsRows - 1) / kWsRows;
+    const long long rows_padded = (long long)BH * nblk * kWsRows;
+    constexpr int RPB = 256 / (D / 8);
+    const long long g1 = (rows_padded + RPB - 1) / RPB;
+    const float c2 = scale * kLog2e;
+    hipLaunchKernelGGL((fa_bwd_delta_kernel<DT, D>), dim3((unsigned)g1), dim3(256), 0, stream,
+                       (const u16 *)o, (const u16 *)dO, lse, ws, N, nblk, rows_padded);
+    const int nkb = (N + kKeysA - 1) / kKeysA;
+    const int nqb = (N + kQB - 1) / kQB;
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D, false, false, false, true>),
+                       dim3((unsigned)((long long)BH * nkb)), dim3(kThreads), 0, stream,
+                       (const u16 *)q, (const u16 *)k, (const u16 *)v, (const u16 *)dO,
+                       (const float *)ws, (u16 *)dk, (u16 *)dv, BH, N, nblk, c2, scale, dr, vl,
+                       wa);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<DT, D, false, false, false, true>),
+                       dim3((unsigned)((long long)BH * nqb)), dim3(kThreads), 0, stream,
+                       (const u16 *)q, (const u16 *)k, (const u16 *)v, (const u16 *)dO,
+                       (const float *)ws, (u16 *)dq, BH, N, nblk, nqb, c2, scale, dr, vl, wa);
+    return hipGetLastError();
 }
 
 typedef hipError_t (*launch_fn)(const void *, const void *, const void *, const void *,
@@ -1010,11 +1127,18 @@ extern "C" size_t fa_bwd_workspace_size(int B, int H, int N)
 namespace {
 
 // Validation and launch shared by fa_bwd and fa_bwd_dropout.
+typedef hipError_t (*launch_window_fn)(const void *, const void *, const void *, const void *,
+                                       const void *, const float *, float *, void *, void *,
+                                       void *, int, int, WindowArgs, float, hipStream_t);
+
+// Validation shared by fa_bwd, fa_bwd_dropout and fa_bwd_window (win: the
+// window sides and the device lengths array, or null).
 fa_status run_bwd(const void *q, const void *k, const void *v, const void *o, const void *dO,
                   const float *lse, float *ws, void *dq, void *dk, void *dv, int B, int H,
                   int N, int d, int causal, float scale, fa_dtype dtype, const DropArgs *drop,
-                  hipStream_t stream)
+                  hipStream_t stream, const WindowArgs *win = nullptr)
 {
+    if (win && (win->wl < -1 || win->wr < -1)) return FA_ERR_INVALID_ARG;
     if (!q || !k || !v || !o || !dO || !lse || !ws || !dq || !dk || !dv)
         return FA_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
@@ -1027,6 +1151,7 @@ fa_status run_bwd(const void *q, const void *k, const void *v, const void *o, co
          (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)ws) & 15)
         return FA_ERR_MISALIGNED;
     if ((uintptr_t)lse & 3) return FA_ERR_MISALIGNED;
+    if (win && ((uintptr_t)win->lens & 3)) return FA_ERR_MISALIGNED;
 
     const long long BH = (long long)B * H;
     const long long nkb = (N + kKeysA - 1) / kKeysA;
@@ -1047,8 +1172,23 @@ fa_status run_bwd(const void *q, const void *k, const void *v, const void *o, co
             if (overlaps(outs[a], outsz[a], ins[b], insz[b])) return FA_ERR_INVALID_ARG;
         for (int b = a + 1; b < 4; ++b)
             if (overlaps(outs[a], outsz[a], outs[b], outsz[b])) return FA_ERR_INVALID_ARG;
+        if (win && win->lens && overlaps(outs[a], outsz[a], win->lens, (size_t)B * 4))
+            return FA_ERR_INVALID_ARG;
     }
 
+    if (win) {
+        // a side of N or more allows every key on that side (kept inside int)
+        const WindowArgs wa = {win->lens, H, win->wl > N ? N : win->wl,
+                               win->wr > N ? N : win->wr};
+        launch_window_fn wf;
+        if (dtype == FA_DTYPE_F16)
+            wf = d == 64 ? launch_window<FA_DTYPE_F16, 64> : launch_window<FA_DTYPE_F16, 128>;
+        else
+            wf = d == 64 ? launch_window<FA_DTYPE_BF16, 64> : launch_window<FA_DTYPE_BF16, 128>;
+        if (wf(q, k, v, o, dO, lse, ws, dq, dk, dv, (int)BH, N, wa, scale, stream) != hipSuccess)
+            return FA_ERR_LAUNCH;
+        return FA_OK;
+    }
     launch_fn fn = (dtype == FA_DTYPE_F16) ? pick<FA_DTYPE_F16>(d, causal, drop != nullptr)
                                            : pick<FA_DTYPE_BF16>(d, causal, drop != nullptr);
     const DropArgs dr = drop ? *drop : DropArgs{0u, 0u, 0u, 256u, 1.f};
@@ -1080,6 +1220,17 @@ extern "C" fa_status fa_bwd_dropout(const void *q, const void *k, const void *v,
                          thr ? 256.f / (float)thr : 0.f};
     return run_bwd(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, causal, scale, dtype, &dr,
                    stream);
+}
+
+extern "C" fa_status fa_bwd_window(const void *q, const void *k, const void *v, const void *o,
+                                   const void *dO, const float *lse, float *ws, void *dq,
+                                   void *dk, void *dv, int B, int H, int N, int d,
+                                   int window_left, int window_right, const int *seqlens,
+                                   float scale, fa_dtype dtype, hipStream_t stream)
+{
+    const WindowArgs win = {seqlens, H, window_left, window_right};
+    return run_bwd(q, k, v, o, dO, lse, ws, dq, dk, dv, B, H, N, d, 0, scale, dtype, nullptr,
+                   stream, &win);
 }
 
 extern "C" size_t fa_bwd_varlen_workspace_size(int B, int H, int total)

@@ -941,6 +941,12 @@ extern "C" fa_status fa_fwd_window(const void *q, const void *k, const void *v, 
                                    fa_dtype dtype, hipStream_t stream)
 {
     if (window_left < -1 || window_right < -1) return FA_ERR_INVALID_ARG;
+    // a side of N or more allows every key on that side: clamp it to N so
+    // the kernel's row +- side arithmetic stays far inside int
+    if (N > 0) {
+        window_left = window_left > N ? N : window_left;
+        window_right = window_right > N ? N : window_right;
+    }
     // the unwindowed and the causal case without lengths run the tuned kernels
     int mode = 2;
     if (!seqlens && window_left == -1 && window_right == -1) mode = 0;

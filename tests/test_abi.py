@@ -326,3 +326,24 @@ def test_varlen_bwd_unsupported_and_misaligned():
     assert vbcall(ws=WS + 4) == fa.FA_ERR_MISALIGNED
     assert vbcall(dk=DK + 8) == fa.FA_ERR_MISALIGNED
     assert vbcall(lse=L + 1) == fa.FA_ERR_MISALIGNED
+
+
+def wbcall(q=Q, k=K, v=V, o=O, do=DO, lse=L, ws=WS, dq=DQ, dk=DK, dv=DV, B=1, H=1, N=64,
+           d=128, wl=16, wr=0, lens=LENS, scale=0.125, dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_bwd_window(q, k, v, o, do, lse, ws, dq, dk, dv, B, H, N, d, wl, wr, lens,
+                            scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [dict(wl=-2), dict(wr=-3), dict(q=0), dict(ws=0), dict(B=0),
+                                dict(N=0), dict(scale=math.inf), dict(dtype=4),
+                                dict(dq=LENS), dict(ws=LENS - 16), dict(dk=Q + 64),
+                                dict(ws=DO)])
+def test_window_bwd_invalid(kw):
+    assert wbcall(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_window_bwd_unsupported_and_misaligned():
+    assert wbcall(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert wbcall(lens=LENS + 2) == fa.FA_ERR_MISALIGNED
+    assert wbcall(dv=DV + 8) == fa.FA_ERR_MISALIGNED
+    assert wbcall(ws=WS + 4) == fa.FA_ERR_MISALIGNED
