@@ -207,7 +207,7 @@ __device__ __forceinline__ int acc_row(int r, int hh) {
 // v_permlane32_swap: swap(x, x) yields [x_lo, x_lo] and [x_hi, x_hi].
 __device__ __forceinline__ float half_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float half_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -312,7 +312,10 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;       // wave index (kRowsPerWave query rows each)
+    // wave index (kRowsPerWave query rows each).  At d = 128 it is held in a
+    // scalar register, so tile-load addressing stays on the scalar unit (at
+    // d = 64 that measured no faster)
+    const int w = D == 128 ? __builtin_amdgcn_readfirstlane(tid >> 6) : (tid >> 6);
     const int l32 = lane & 31;
     const int hh = lane >> 5;
 
@@ -423,14 +426,19 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     // 2^30 (>= every head's size) makes every lane out of range, which fills
     // the LDS destination with zeros without touching memory.
     static_assert(T::kLoads % kWaves == 0, "whole loads per wave");
+    // Load li covers rows li*kRowsPerLoad.., and kWaves*kRowsPerLoad is a
+    // multiple of 16, so a lane's swizzled byte offset inside its 1 KB does
+    // not depend on jn: it is computed once (kl / vl) and each load adds the
+    // wave-uniform part base + li*1024.
+    static_assert((kWaves * T::kRowsPerLoad) % 16 == 0, "swizzle invariant over loads");
+    const int lrow = w * T::kRowsPerLoad + lane / T::kChunks;   // row of load jn = 0
+    const int kl = (lane / T::kChunks) * T::kRowBytes + (((lane % T::kChunks) ^ T::kswz(lrow)) << 4);
+    const int vl = (lane / T::kChunks) * T::kRowBytes + (((lane % T::kChunks) ^ T::vswz(lrow)) << 4);
     auto issue_one = [&](int n, auto kbuf, auto vbuf, int base) {
         const bool is_v = n >= T::kLoadsPerWave;
         const int jn = is_v ? n - T::kLoadsPerWave : n;
         const int li = jn * kWaves + w;
-        const int row = li * T::kRowsPerLoad + lane / T::kChunks;
-        const int pc = lane % T::kChunks;
-        const int lc = pc ^ (is_v ? T::vswz(row) : T::kswz(row));
-        const int off = base + row * T::kRowBytes + lc * 16;
+        const int off = (base + li * 1024) + (is_v ? vl : kl);
         if (is_v)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rv, (LDS void *)(bufp(vbuf) + li * 1024), 16, off, 0, 0, 0);
@@ -455,12 +463,27 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         }
     }
 
+    // Per-lane V read addresses of each V buffer, formed once and held in
+    // registers (the empty asm keeps the compiler from re-forming them): every
+    // transposing read is then one of them plus an immediate offset.  Formed
+    // per read, each cost a VALU op, as the V buffers lie beyond the 64 KB
+    // reach of the offset field.
+    // (At d = 64 the tiles are half as large and this measured slower.)
+    const LDS unsigned char *vad[2][DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        vad[0][db] = bufp(Buf<2>{}) + voff[db];
+        vad[1][db] = bufp(Buf<3>{}) + voff[db];
+        if constexpr (D == 128) asm volatile("" : "+v"(vad[0][db]), "+v"(vad[1][db]));
+    }
+
     int sub = 0;   // which kBC-key half of the LDS tile the current step uses
     auto kfrag = [&](auto buf, int kb, int kk) -> u16x8 {
         return *(const LDS u16x8 *)(bufp(buf) + (sub * kBC + kb * 32) * T::kRowBytes + koff[kk]);
     };
     auto vfrag = [&](auto buf, int db, int kk) -> u16x8 {
-        const LDS unsigned char *p = bufp(buf) + (sub * kBC + kk * 16) * T::kRowBytes + voff[db];
+        constexpr int vb = decltype(buf)::value - 2;
+        const LDS unsigned char *p = vad[vb][db] + (sub * kBC + kk * 16) * T::kRowBytes;
         const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4 *)p);
         const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (LDS s16x4 *)(p + 8 * T::kRowBytes));
