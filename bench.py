@@ -8,13 +8,16 @@ to stderr.
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10]
                   [--workload n8k_causal_peaky] [--secondary n4k_causal]
+                  [--extra n4k_full,n8k_full,n16k_d64]
                   [--backward n8k_causal_peaky] [--window n8k_causal_peaky:1023:0]
                   [--split n4k_h4_causal:4] [--dropout n8k_causal_peaky:0.1]
                   [--varlen 32:128:8:512:8192] [--spinup 0.3]
                   [--no-cold] [--no-cpu-baseline] [--mode copy]
 
 The headline workload is B=1 H=32 N=8192 d=128 bf16 causal with Q,K x3;
-B=2 H=16 N=4096 d=128 bf16 causal is reported beside it, and the backward
+B=2 H=16 N=4096 d=128 bf16 causal is reported beside it, the non-causal
+B=2 H=16 N=4096 and B=1 H=32 N=8192 d=128 bf16 forwards and the few-head
+B=1 H=4 N=16384 d=64 fp16 forward under "extra", and the backward
 pass (fa_bwd) of the headline workload under "backward", and a sliding-window
 forward and backward (fa_fwd_window, fa_bwd_window; each query sees the 1024 keys
 ending at itself) under "window", and fa_fwd against fa_fwd_split on a few-head shape under "split", and
@@ -575,6 +578,9 @@ def main() -> int:
     ap.add_argument("--workload", default="n8k_causal_peaky")
     ap.add_argument("--secondary", default="n4k_causal",
                     help="second workload reported beside the headline ('none' to skip)")
+    ap.add_argument("--extra", default="n4k_full,n8k_full,n16k_d64",
+                    help="comma-separated forward workloads reported under 'extra' "
+                         "('none' to skip)")
     ap.add_argument("--backward", default="n8k_causal_peaky",
                     help="workload whose backward pass is reported beside ('none' to skip)")
     ap.add_argument("--window", default="n8k_causal_peaky:1023:0",
@@ -687,6 +693,21 @@ def main() -> int:
                              "kernel_us_mean": round(r2["kernel_ms_mean"] * 1e3, 2),
                              "frac": round(a2 / PEAK_BF16_TFLOPS, 4)}
         del r2
+
+    if args.extra and args.extra != "none":
+        line["extra"] = []
+        for name in args.extra.split(","):
+            we = WORKLOADS[name]
+            re_ = time_workload(we, args.steps, args.warmup)
+            ae = we.flops / (re_["kernel_ms_mean"] * 1e-3) / 1e12
+            log(f"bench: extra {we.name} kernel mean {re_['kernel_ms_mean']*1e3:.1f} us, "
+                f"{ae:.1f} TFLOP/s ({100*ae/PEAK_BF16_TFLOPS:.1f}% of peak)")
+            line["extra"].append({"workload": we.name, "B": we.B, "H": we.H, "N": we.N, "d": we.d,
+                                  "dtype": we.dtype, "causal": we.causal,
+                                  "kernel_us_mean": round(re_["kernel_ms_mean"] * 1e3, 2),
+                                  "tflops": round(ae, 2),
+                                  "frac": round(ae / PEAK_BF16_TFLOPS, 4)})
+            del re_
 
     if args.backward and args.backward != "none":
         wb = WORKLOADS[args.backward]

@@ -467,8 +467,11 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     // registers (the empty asm keeps the compiler from re-forming them): every
     // transposing read is then one of them plus an immediate offset.  Formed
     // per read, each cost a VALU op, as the V buffers lie beyond the 64 KB
-    // reach of the offset field.
-    // (At d = 64 the tiles are half as large and this measured slower.)
+    // reach of the offset field.  The price: the compiler no longer knows
+    // which buffer such a read touches, so it waits for this wave's in-flight
+    // tile loads before the first V read of a step; those loads were issued a
+    // whole QK^T earlier and have landed, and the trade measured faster.
+    // (At d = 64 the tiles are half as large and holding them measured slower.)
     const LDS unsigned char *vad[2][DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {

@@ -40,4 +40,7 @@ def test_bench_json_line():
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
     for rec in ("secondary", "backward", "window", "split", "dropout", "varlen", "cold"):
         assert rec in j, rec
+    assert [e["workload"] for e in j["extra"]] == ["n4k_full", "n8k_full", "n16k_d64"]
+    for e in j["extra"]:
+        assert e["tflops"] > 0 and abs(e["frac"] - e["tflops"] / 2500.0) < 1e-3
     assert j["parity_sample"]["floor_aware_ok"]

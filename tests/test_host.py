@@ -76,9 +76,9 @@ def test_bench_refuses_more_than_one_gpu(n):
 def test_bench_help_names_every_option():
     r = _bench("--help")
     assert r.returncode == 0
-    for opt in ("--gpus", "--steps", "--warmup", "--workload", "--backward", "--window",
-                "--split", "--dropout", "--varlen", "--spinup", "--no-cold",
-                "--no-cpu-baseline"):
+    for opt in ("--gpus", "--steps", "--warmup", "--workload", "--secondary", "--extra",
+                "--backward", "--window", "--split", "--dropout", "--varlen", "--spinup",
+                "--no-cold", "--no-cpu-baseline"):
         assert opt in r.stdout, opt
 
 
@@ -132,3 +132,15 @@ def test_bench_reads_the_marked_engine_clock(tmp_path):
     assert bench.read_sclk_mhz(str(f)) == 2400
     f.write_text("0: 500Mhz\n1: 2400Mhz\n")
     assert bench.read_sclk_mhz(str(f)) is None
+
+
+def test_bench_extra_workloads_exist():
+    """The default extra records name workloads of the input recipe: the
+    non-causal N4096 / N8192 d128 bf16 points and the few-head d64 one."""
+    from io_aware_transformer_amd.inputs import WORKLOADS
+    src = (ROOT / "bench.py").read_text()
+    assert '"--extra", default="n4k_full,n8k_full,n16k_d64"' in src
+    for name in ("n4k_full", "n8k_full", "n16k_d64"):
+        w = WORKLOADS[name]
+        assert w.d in (64, 128) and w.causal is False
+    assert (WORKLOADS["n4k_full"].N, WORKLOADS["n8k_full"].N) == (4096, 8192)
