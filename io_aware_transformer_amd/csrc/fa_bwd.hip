@@ -248,7 +248,9 @@ __device__ __forceinline__ void load_rows(const __amdgpu_buffer_rsrc_t &r, LDS u
 
 // ---------------------------------------------------------------- delta
 
-// ws block (bh, n / 32): [32 x lse*log2e][32 x D]; rows n >= N get (+inf, 0).
+// ws block (bh, n / 32): [32 x lse*log2e][32 x -D]; rows n >= N get (+inf, 0).
+// -D is stored because both gradient kernels start their dP' accumulators at
+// -D: the dK/dV kernel loads it from LDS straight into the accumulator.
 template <int DT, int D>
 __global__ __launch_bounds__(256)
 void fa_bwd_delta_kernel(const u16 *__restrict__ O, const u16 *__restrict__ dO,
@@ -280,7 +282,7 @@ void fa_bwd_delta_kernel(const u16 *__restrict__ O, const u16 *__restrict__ dO,
         float *blk = WS + (size_t)(r / kWsRows) * (2 * kWsRows);
         const int i = (int)(r % kWsRows);
         blk[i] = valid ? LSE[(size_t)bh * N + n] * kLog2e : __builtin_inff();
-        blk[kWsRows + i] = acc;
+        blk[kWsRows + i] = -acc;
     }
 }
 
@@ -318,7 +320,7 @@ void fa_bwd_delta_varlen_kernel(const u16 *__restrict__ O, const u16 *__restrict
         float *blk = WS + idx / kWsRows * (2 * kWsRows);
         const int i = (int)(idx % kWsRows);
         blk[i] = valid ? LSE[sq.row0 + r] * kLog2e : __builtin_inff();
-        blk[kWsRows + i] = acc;
+        blk[kWsRows + i] = -acc;
     }
 }
 
@@ -348,13 +350,17 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     constexpr int TL = QTB / 1024;             // 1 KB loads per Q or dO tile
     static_assert(TL % kWaves == 0, "tile loads split evenly over the waves");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char vs[kKeysA * T::kRowBytes];
+    // The per-step Q / dO tiles should sit in the first 64 KB, so that every
+    // read of them is a lane offset plus an immediate (the reach of the
+    // ds_read offset field); LDS objects are placed by decreasing alignment,
+    // so the work-group's V rows (read at fixed addresses) get a smaller one.
     __shared__ __attribute__((aligned(1024))) unsigned char q0s[QTB];
     __shared__ __attribute__((aligned(1024))) unsigned char q1s[QTB];
     __shared__ __attribute__((aligned(1024))) unsigned char o0s[QTB];
     __shared__ __attribute__((aligned(1024))) unsigned char o1s[QTB];
     __shared__ __attribute__((aligned(256))) float w0s[2 * kQT];
     __shared__ __attribute__((aligned(256))) float w1s[2 * kQT];
+    __shared__ __attribute__((aligned(512))) unsigned char vs[kKeysA * T::kRowBytes];
     // dropout bytes of one query tile, per wave: [step 2][key 32][query
     // half 2][g 4] words
     __shared__ __attribute__((aligned(1024))) unsigned zs[DROP ? kWaves * 512 : 1];
@@ -558,17 +564,17 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // dP' = dO V^T - D: the accumulator starts at -D of the lane's rows
-        // (at 0 under dropout, where D enters after the keep factor)
+        // dP' = dO V^T - D: the accumulator starts at -D of the lane's rows,
+        // as stored (at 0 under dropout, where D enters after the keep factor)
         f32x16 dp;
         if constexpr (DROP) {
             dp = f32x16{};
         } else {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const f32x4 dv4 = *(const LDS f32x4 *)(wb + kWsRows + 8 * g + 4 * hh);
+                const f32x4 nd4 = *(const LDS f32x4 *)(wb + kWsRows + 8 * g + 4 * hh);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dp[4 * g + e] = -dv4[e];
+                for (int e = 0; e < 4; ++e) dp[4 * g + e] = nd4[e];
             }
         }
         {
@@ -606,8 +612,8 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x4 l4 = *(const LDS f32x4 *)(wb + 8 * g + 4 * hh);
-            f32x4 d4;
-            if constexpr (DROP) d4 = *(const LDS f32x4 *)(wb + kWsRows + 8 * g + 4 * hh);
+            f32x4 nd4;   // -D of the four rows
+            if constexpr (DROP) nd4 = *(const LDS f32x4 *)(wb + kWsRows + 8 * g + 4 * hh);
             float p[4], ds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -622,7 +628,7 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                 if constexpr (DROP) {
                     // dS = P (Z dP - D), and P Z for the dV product
                     const float zf = ((zb[g] >> (8 * e)) & 0xffu) < dr.thr ? dr.fscale : 0.f;
-                    ds[e] = p[e] * fmaf(zf, dp[4 * g + e], -d4[e]);
+                    ds[e] = p[e] * fmaf(zf, dp[4 * g + e], nd4[e]);
                     p[e] *= zf;
                 } else {
                     ds[e] = p[e] * dp[4 * g + e];
@@ -790,11 +796,11 @@ void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         of[kk] = __builtin_bit_cast(u16x8, __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0));
     }
     // this lane's row statistics (rows past N read as +inf and 0)
-    float l2 = __builtin_inff(), dd = 0.f;
+    float l2 = __builtin_inff(), nd = 0.f;   // lse log2(e) and -D of the row
     if (qrow < N) {
         const float *blk = WS + (ws_blk0 + qrow / kWsRows) * (2 * kWsRows);
         l2 = blk[qrow % kWsRows];
-        dd = blk[kWsRows + qrow % kWsRows];
+        nd = blk[kWsRows + qrow % kWsRows];
     }
 
     const int n_kt32 = (N + 31) / 32;
@@ -873,7 +879,7 @@ void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         // i, V for odd) read from LDS AH MFMAs ahead, the interleave pinned
         f32x16 s = {}, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = DROP ? 0.f : -dd;
+        for (int r = 0; r < 16; ++r) dp[r] = DROP ? 0.f : nd;
         {
             constexpr int NR = 2 * KT;
             constexpr int AH = 3;
@@ -919,7 +925,7 @@ void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                 }
                 if constexpr (DROP) {
                     const float zf = ((zb[g] >> (8 * e)) & 0xffu) < dr.thr ? dr.fscale : 0.f;
-                    ds[e] = __builtin_amdgcn_exp2f(x) * fmaf(zf, dp[4 * g + e], -dd);
+                    ds[e] = __builtin_amdgcn_exp2f(x) * fmaf(zf, dp[4 * g + e], nd);
                 } else {
                     ds[e] = __builtin_amdgcn_exp2f(x) * dp[4 * g + e];
                 }
