@@ -609,22 +609,33 @@ void fa_bwd_dkdv_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         u32x4 zb;
         if constexpr (DROP) zb = drop_bytes(u);
         u32x4 pp[2], dsp[2];
+        float xv[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x4 l4 = *(const LDS f32x4 *)(wb + 8 * g + 4 * hh);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xv[4 * g + e] = fmaf(s[4 * g + e], c2, -l4[e]);
+        }
+        // the mask only on masked steps: a branch on the wave-uniform flag,
+        // so that the other steps carry none of its selects
+        if (__builtin_amdgcn_readfirstlane((int)diag)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = 8 * (r >> 2) + 4 * hh + (r & 3);   // query qs + m
+                bool masked;
+                if constexpr (WIN) masked = !window_allows(wa, lb, qs + m, kw + l32);
+                else masked = l32 > m;
+                if (masked) xv[r] = neg_inf();
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
             f32x4 nd4;   // -D of the four rows
             if constexpr (DROP) nd4 = *(const LDS f32x4 *)(wb + kWsRows + 8 * g + 4 * hh);
             float p[4], ds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float x = fmaf(s[4 * g + e], c2, -l4[e]);
-                if constexpr (WIN) {
-                    if (diag && !window_allows(wa, lb, qs + 8 * g + 4 * hh + e, kw + l32))
-                        x = neg_inf();
-                } else if (diag && l32 > 8 * g + 4 * hh + e) {
-                    x = neg_inf();
-                }
-                p[e] = __builtin_amdgcn_exp2f(x);
+                p[e] = __builtin_amdgcn_exp2f(xv[4 * g + e]);
                 if constexpr (DROP) {
                     // dS = P (Z dP - D), and P Z for the dV product
                     const float zf = ((zb[g] >> (8 * e)) & 0xffu) < dr.thr ? dr.fscale : 0.f;
@@ -911,18 +922,27 @@ void fa_bwd_dq_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             zb = philox4x32_10((unsigned)qrow, (unsigned)(2 * (ks0 / 32) + hh), (unsigned)bh,
                                dr.offset, dr.seed_lo, dr.seed_hi);
         u32x4 dsp[2];
+        float xv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xv[r] = fmaf(s[r], c2, -l2);
+        // the mask only on masked steps: a branch on the wave-uniform flag,
+        // so that the other steps carry none of its compares and selects
+        if (__builtin_amdgcn_readfirstlane((int)diag)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = ks0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                bool masked;
+                if constexpr (WIN) masked = !window_allows(wa, lb, qrow, key);
+                else masked = key > qrow;
+                if (masked) xv[r] = neg_inf();
+            }
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             float ds[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float x = fmaf(s[4 * g + e], c2, -l2);
-                if constexpr (WIN) {
-                    if (diag && !window_allows(wa, lb, qrow, ks0 + 8 * g + 4 * hh + e))
-                        x = neg_inf();
-                } else if (diag && ks0 + 8 * g + 4 * hh + e > qrow) {
-                    x = neg_inf();
-                }
+                const float x = xv[4 * g + e];
                 if constexpr (DROP) {
                     const float zf = ((zb[g] >> (8 * e)) & 0xffu) < dr.thr ? dr.fscale : 0.f;
                     ds[e] = __builtin_amdgcn_exp2f(x) * fmaf(zf, dp[4 * g + e], nd);
