@@ -29,9 +29,12 @@
 //    query column (lane l and l+32 share the column).  Row max and row sum are
 //    per-lane work plus one v_permlane32_swap, and the fp32 scores, once
 //    rounded to 16 bits, are already the B operand of the P.V product.
-//  * Every accumulator lives in VGPRs (about 210 per lane), so two waves
-//    share each SIMD and the MFMA work of one overlaps the softmax VALU work
-//    of the other.  One 8-wave work-group fills a CU (128 KB of LDS); the
+//  * Every accumulator lives in VGPRs (about 175 per lane), so two waves
+//    share each SIMD and one issues while the other waits on LDS or on the
+//    matrix pipe.  (Measured: MFMA and VALU instructions of a SIMD do not
+//    execute at once, from one wave or two, so the softmax VALU work adds to
+//    the MFMA time; fewer VALU instructions per score is what speeds the
+//    kernel up.)  One 8-wave work-group fills a CU (128 KB of LDS); the
 //    128-key tiles halve the barriers per key against 64-key tiles.
 //    Measured on MI355X and rejected: 4-wave work-groups (two per CU), a
 //    12-wave group at three waves per SIMD, an in-wave software pipeline
