@@ -83,6 +83,7 @@ namespace {
 typedef unsigned short u16;
 typedef u16 u16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -612,15 +613,20 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                     rs[h] = (g == 0) ? a : rs[h] + a;
                 }
                 if constexpr (DROP) {
-                    // register r holds key 8(r/4) + 4hh + r%4: byte r of the call
-                    float z[2];
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const int r = r0 + 2 * h + t;
-                        const unsigned byte = (rnd[kb][r >> 2] >> (8 * (r & 3))) & 0xffu;
-                        z[t] = byte < dr.thr ? p[2 * h + t] : 0.f;
-                    }
-                    pk[2 * kb + (r0 >> 3)][h] = E::pack2(z[0], z[1]);
+                    // register r holds key 8(r/4) + 4hh + r%4: byte r of the
+                    // call.  The pair's two bytes (r = r0 + 2h, r0 + 2h + 1)
+                    // are spread into the two 16-bit halves of a word; byte -
+                    // thr is negative exactly for a kept weight, so the
+                    // arithmetic shift by 15 turns each half into an all-ones
+                    // (kept) or all-zeros (dropped) mask of its packed weight.
+                    // (v_perm_b32(a, b, sel): selector byte 0-3 takes byte
+                    // 0-3 of b, 0x0c a zero byte)
+                    const unsigned wd = rnd[kb][(r0 >> 2) + (h >> 1)];
+                    const unsigned two = __builtin_amdgcn_perm(0u, wd, (h & 1) ? 0x0c030c02u : 0x0c010c00u);
+                    s16x2 keep = __builtin_bit_cast(s16x2, two) - (short)dr.thr;
+                    keep = keep >> 15;
+                    pk[2 * kb + (r0 >> 3)][h] =
+                        E::pack2(p[2 * h], p[2 * h + 1]) & __builtin_bit_cast(unsigned, keep);
                 } else {
                     const unsigned pr = E::pack2(p[2 * h], p[2 * h + 1]);
                     rh[h] = E::sum2(pr, (g == 0) ? 0.f : rh[h]);
