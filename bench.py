@@ -536,6 +536,11 @@ def cpu_baseline(w, inputs, outputs, target_s: float):
         "strict_ok": bool(err.max() <= tol and lerr.max() <= 1e-3),
         "floor_aware_ok": bool(np.all(err <= tol + floor) and lerr.max() <= 1e-3),
         "n_rounding_floor_over_tol": int(np.count_nonzero(floor > tol)),
+        "n_over_tol": int(np.count_nonzero(err > tol)),
+        # the kernel's own error beyond the rounding floor of the 16-bit
+        # output; the floor-aware check passes while this stays <= tol
+        "max_err_beyond_floor": float((err - floor).max()),
+        "tol": tol,
     }
 
 
@@ -794,7 +799,15 @@ def main() -> int:
             f"sampled parity max|dO|={par['max_err_o']:.2e} max|dlse|={par['max_err_lse']:.2e}")
         line["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
         line["cpu_baseline"]["cpu_model"] = cb["cpu_model"]
+        line["cpu_baseline"]["host_cpus"] = os.cpu_count()
         line["parity_sample"] = par
+        if not par["floor_aware_ok"]:
+            # a fast but wrong kernel yields no headline: the line is printed
+            # for the record, marked invalid, and the run fails
+            line["valid"] = False
+            print(json.dumps(line), flush=True)
+            log("bench: PARITY FAILED on the sampled rows; the measurement is invalid")
+            return 3
     print(json.dumps(line), flush=True)
     return 0
 

@@ -261,12 +261,19 @@ def attention_backward(q, k, v, o, lse, do, causal: bool = False, scale: float |
     given the forward's o and lse.  Allocates the outputs and the workspace;
     raises FaError on a non-zero status."""
     import torch
-    dt = FA_DTYPE_F16 if q.dtype == torch.float16 else FA_DTYPE_BF16
     if q.dtype not in (torch.float16, torch.bfloat16):
         raise TypeError("q, k, v must be float16 or bfloat16")
+    dt = FA_DTYPE_F16 if q.dtype == torch.float16 else FA_DTYPE_BF16
+    if q.dim() != 4 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B,H,N,d] tensor")
     for t in (k, v, o, do):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
             raise ValueError("k, v, o, do must be contiguous and match q")
+    # the kernel reads B*H*N fp32 row statistics from lse's first address
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32 (the forward's log-sum-exp)")
+    if tuple(lse.shape) != tuple(q.shape[:3]) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous [B,H,N] tensor")
     if any(t.device.type != "cuda" or t.device != q.device for t in (q, k, v, o, lse, do)):
         raise ValueError("all tensors must be on one GPU (there is no CPU path)")
     B, H, N, d = q.shape

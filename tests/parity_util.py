@@ -70,6 +70,9 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype: str) -> dict:
         "floor_max": float(floor.max(initial=0.0)),
         "n_floor_over_tol": int(np.count_nonzero(floor > tol)),
         "n_over_tol": int(np.count_nonzero(err > tol)),
+        # the kernel's own error beyond the rounding floor: how much of the
+        # tolerance the floor-aware check leaves unused (tol minus this)
+        "max_err_beyond_floor": float((err - floor).max(initial=0.0)),
         "tol": tol,
     }
 

@@ -144,3 +144,26 @@ def test_bench_extra_workloads_exist():
         w = WORKLOADS[name]
         assert w.d in (64, 128) and w.causal is False
     assert (WORKLOADS["n4k_full"].N, WORKLOADS["n8k_full"].N) == (4096, 8192)
+
+
+def test_attention_backward_validates_lse():
+    """attention_backward checks the forward's row statistics before any
+    launch: the kernel reads B*H*N contiguous fp32 values from lse."""
+    import io_aware_transformer_amd as fa
+    q = torch.zeros((2, 3, 8, 64), dtype=torch.bfloat16)
+    good = torch.zeros((2, 3, 8), dtype=torch.float32)
+    with pytest.raises(TypeError, match="lse must be float32"):
+        fa.attention_backward(q, q, q, q, good.half(), q)
+    with pytest.raises(TypeError, match="lse must be float32"):
+        fa.attention_backward(q, q, q, q, good.double(), q)
+    with pytest.raises(ValueError, match=r"lse must be a contiguous \[B,H,N\]"):
+        fa.attention_backward(q, q, q, q, torch.zeros((2, 3, 7)), q)
+    with pytest.raises(ValueError, match=r"lse must be a contiguous \[B,H,N\]"):
+        fa.attention_backward(q, q, q, q, torch.zeros((6, 8)), q)
+    with pytest.raises(ValueError, match=r"lse must be a contiguous \[B,H,N\]"):
+        fa.attention_backward(q, q, q, q, torch.zeros((2, 8, 3)).transpose(1, 2), q)
+    with pytest.raises(ValueError, match=r"\[B,H,N,d\]"):
+        fa.attention_backward(q[0], q[0], q[0], q[0], good[0], q[0])
+    # a well-formed call gets as far as the device check
+    with pytest.raises(ValueError, match="no CPU path"):
+        fa.attention_backward(q, q, q, q, good, q)
