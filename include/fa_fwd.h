@@ -48,7 +48,9 @@ typedef enum {
     FA_ERR_UNSUPPORTED = -2,  /* d not 64 or 128, or N above FA_MAX_N */
     FA_ERR_MISALIGNED = -3,   /* q, k, v or o not 16-byte aligned, lse not
                                  4-byte aligned */
-    FA_ERR_LAUNCH = -4        /* the kernel launch was rejected by HIP */
+    FA_ERR_LAUNCH = -4,       /* the kernel launch was rejected by HIP */
+    FA_ERR_SCRATCH = -5       /* fa_fwd_split_noalloc: the partials need more
+                                 than FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;
 
 typedef enum { FA_DTYPE_F16 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
@@ -150,6 +152,31 @@ fa_status fa_fwd_split(const void *q, const void *k, const void *v, void *o,
                        float *lse, int B, int H, int N, int d, int causal,
                        float scale, int num_splits, float *ws, fa_dtype dtype,
                        hipStream_t stream);
+
+/* Size of the static per-device scratch of fa_fwd_split_noalloc. */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* fa_fwd_split for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, and harnesses that forbid
+ * hipMalloc.  It takes no workspace argument and calls no allocator.  The
+ * split partials go to a file-scope device array of FA_NOALLOC_SCRATCH_BYTES
+ * bytes instead, which every device the library runs on holds from its first
+ * call on that device (whose address the library looks up then) until the
+ * process ends.  Results are bit-identical to fa_fwd_split with the same
+ * arguments.
+ *   stream  must belong to the current device (0 = its null stream)
+ * Errors: as fa_fwd_split, and FA_ERR_SCRATCH (nothing launched) when
+ * fa_fwd_split_workspace_size(B, H, N, d, num_splits) exceeds
+ * FA_NOALLOC_SCRATCH_BYTES; FA_ERR_INVALID_ARG for a stream of another
+ * device; FA_ERR_LAUNCH if HIP cannot report the current device, the stream's
+ * device or the scratch address.  Every call on one device shares that
+ * device's array, and the kernels overwrite every entry they later read, so
+ * calls ordered on one stream need no clearing in between; calls that can
+ * overlap on one device (different streams, no ordering) race on it. */
+fa_status fa_fwd_split_noalloc(const void *q, const void *k, const void *v,
+                               void *o, float *lse, int B, int H, int N, int d,
+                               int causal, float scale, int num_splits,
+                               fa_dtype dtype, hipStream_t stream);
 
 /* Forward pass with dropout on the attention weights, the operation that
  * "FlashAttention V2 核心原理与架构设计" (wmrh.cn) fuses into the kernel

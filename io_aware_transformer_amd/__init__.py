@@ -14,6 +14,8 @@ C entry points mirrored here with the same names and argument order:
                 scale, dtype, stream) -> status
   fa_fwd_split(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, ws,
                dtype, stream) -> status
+  fa_fwd_split_noalloc(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits,
+                       dtype, stream) -> status
   fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, total, max_seqlen, d,
                 causal, scale, dtype, stream) -> status
   fa_fwd_split_workspace_size(B, H, N, d, num_splits) -> bytes
@@ -45,14 +47,17 @@ FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_MISALIGNED = -3
 FA_ERR_LAUNCH = -4
+FA_ERR_SCRATCH = -5
 FA_DTYPE_F16 = 0
 FA_DTYPE_BF16 = 1
 
 EXPORTED = ("fa_fwd_f16", "fa_fwd_bf16", "fa_fwd", "fa_fwd_window", "fa_fwd_split",
             "fa_fwd_split_workspace_size", "fa_status_string", "fa_bwd",
             "fa_bwd_workspace_size", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_varlen",
-            "fa_bwd_varlen", "fa_bwd_varlen_workspace_size", "fa_bwd_window")
+            "fa_bwd_varlen", "fa_bwd_varlen_workspace_size", "fa_bwd_window",
+            "fa_fwd_split_noalloc")
 FA_MAX_SPLITS = 64
+FA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -90,6 +95,8 @@ def load():
     lib.fa_fwd_window.restype = ctypes.c_int
     lib.fa_fwd_split.argtypes = [p, p, p, p, p, i, i, i, i, i, f, i, p, i, p]
     lib.fa_fwd_split.restype = ctypes.c_int
+    lib.fa_fwd_split_noalloc.argtypes = [p, p, p, p, p, i, i, i, i, i, f, i, i, p]
+    lib.fa_fwd_split_noalloc.restype = ctypes.c_int
     lib.fa_fwd_split_workspace_size.argtypes = [i, i, i, i, i]
     lib.fa_fwd_split_workspace_size.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [p] * 10 + [i, i, i, i, i, f, i, p]
@@ -158,6 +165,13 @@ def fa_fwd_split(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, ws, dty
     return load().fa_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
                                int(N), int(d), int(causal), float(scale), int(num_splits),
                                _ptr(ws), int(dtype), _stream(stream))
+
+
+def fa_fwd_split_noalloc(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits, dtype,
+                         stream=None) -> int:
+    return load().fa_fwd_split_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B),
+                                       int(H), int(N), int(d), int(causal), float(scale),
+                                       int(num_splits), int(dtype), _stream(stream))
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, total, max_seqlen, d, causal, scale,

@@ -75,6 +75,7 @@
 #include <stdint.h>
 #include <math.h>
 #include <limits.h>
+#include <mutex>
 
 #include "fa_fwd.h"
 
@@ -1023,6 +1024,64 @@ extern "C" fa_status fa_fwd_split(const void *q, const void *k, const void *v, v
                       dtype, stream, nseg, kseg, po, pl);
 }
 
+// Split partials of fa_fwd_split_noalloc: each device holds its own copy.
+// Host code never passes this name to a kernel (on the host it is only a
+// stand-in); it uses the device address that hipGetSymbolAddress returns.
+static __device__ __align__(256) float scratch[FA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+float *g_scratch[kMaxDevices];   // device address of `scratch`, per device
+
+// The address of `scratch` on device `dev`, which must be current; looked
+// up on the first call for that device and kept.
+hipError_t scratch_address(int dev, float **out)
+{
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch[dev] = (float *)ptr;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" fa_status fa_fwd_split_noalloc(const void *q, const void *k, const void *v,
+                                          void *o, float *lse, int B, int H, int N, int d,
+                                          int causal, float scale, int num_splits,
+                                          fa_dtype dtype, hipStream_t stream)
+{
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (num_splits < 1 || num_splits > FA_MAX_SPLITS) return FA_ERR_INVALID_ARG;
+    const fa_status vs = validate_fwd(q, k, v, o, lse, B, H, N, d, nullptr, scale, dtype);
+    if (vs != FA_OK) return vs;
+    if (fa_fwd_split_workspace_size(B, H, N, d, num_splits) > FA_NOALLOC_SCRATCH_BYTES)
+        return FA_ERR_SCRATCH;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return FA_ERR_LAUNCH;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return FA_ERR_LAUNCH;
+        if (sdev != dev) return FA_ERR_INVALID_ARG;
+    }
+    float *ws = nullptr;
+    if (scratch_address(dev, &ws) != hipSuccess) return FA_ERR_LAUNCH;
+    const int kseg = split_kseg(N, num_splits);
+    const int nseg = (N + kseg - 1) / kseg;
+    float *po = ws;
+    float *pl = ws + (size_t)nseg * B * H * N * d;
+    return launch_fwd(q, k, v, o, lse, B, H, N, d, 3, -1, causal ? 0 : -1, nullptr, scale,
+                      dtype, stream, nseg, kseg, po, pl);
+}
+
 extern "C" fa_status fa_fwd_dropout(const void *q, const void *k, const void *v, void *o,
                                     float *lse, int B, int H, int N, int d, int causal,
                                     float scale, float p_drop, unsigned long long seed,
@@ -1093,6 +1152,9 @@ extern "C" const char *fa_status_string(int status)
     case FA_ERR_MISALIGNED:
         return "FA_ERR_MISALIGNED: q/k/v/o need 16-byte alignment, lse 4-byte";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: HIP rejected the kernel launch";
+    case FA_ERR_SCRATCH:
+        return "FA_ERR_SCRATCH: the split partials exceed the static scratch "
+               "(FA_NOALLOC_SCRATCH_BYTES); use fa_fwd_split with a workspace";
     default: return "unknown fa_status";
     }
 }

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_cover_every_code():
     for code in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED,
-                 fa.FA_ERR_MISALIGNED, fa.FA_ERR_LAUNCH):
+                 fa.FA_ERR_MISALIGNED, fa.FA_ERR_LAUNCH, fa.FA_ERR_SCRATCH):
         s = fa.fa_status_string(code)
         assert s.startswith(("FA_OK", "FA_ERR_")), s
     assert fa.fa_status_string(7) == "unknown fa_status"
@@ -222,6 +222,32 @@ def test_split_unsupported_and_misaligned():
     assert scall(d=32) == fa.FA_ERR_UNSUPPORTED
     assert scall(ws=SWS + 4) == fa.FA_ERR_MISALIGNED
     assert scall(k=K + 2) == fa.FA_ERR_MISALIGNED
+
+
+def ncall(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=64, d=128, causal=0, scale=0.125, ns=2,
+          dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_fwd_split_noalloc(q, k, v, o, lse, B, H, N, d, causal, scale, ns, dtype, None)
+
+
+@pytest.mark.parametrize("kw", [dict(ns=0), dict(ns=65), dict(causal=3), dict(q=0),
+                                dict(lse=0), dict(N=0), dict(o=Q), dict(scale=float("nan"))])
+def test_split_noalloc_invalid(kw):
+    assert ncall(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_split_noalloc_unsupported_misaligned_and_too_large():
+    assert ncall(d=32) == fa.FA_ERR_UNSUPPORTED
+    assert ncall(k=K + 2) == fa.FA_ERR_MISALIGNED
+    # partials larger than the static scratch: refused before any HIP call
+    far = dict(q=1 << 36, k=2 << 36, v=3 << 36, o=4 << 36, lse=5 << 36)
+    B, H, N, d, ns = 1, 8, 8192, 128, 2
+    assert fa.fa_fwd_split_workspace_size(B, H, N, d, ns) > fa.FA_NOALLOC_SCRATCH_BYTES
+    assert ncall(B=B, H=H, N=N, d=d, ns=ns, **far) == fa.FA_ERR_SCRATCH
+    # the largest problem of one head and one segment that still fits
+    n_fit = fa.FA_NOALLOC_SCRATCH_BYTES // (129 * 4)
+    assert fa.fa_fwd_split_workspace_size(1, 1, n_fit, 128, 1) <= fa.FA_NOALLOC_SCRATCH_BYTES
+    assert fa.fa_fwd_split_workspace_size(1, 1, n_fit + 1, 128, 1) > fa.FA_NOALLOC_SCRATCH_BYTES
+    assert ncall(N=n_fit + 1, ns=1, **far) == fa.FA_ERR_SCRATCH
 
 
 # ---------------------------------------------------------------- dropout
