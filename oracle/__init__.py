@@ -52,6 +52,11 @@ Functions and what pins them (tests/test_oracle.py):
                   ([P-baidu] §8 mask kinds) -- the unmasked and causal cases
                   of attn_fwd, padded batches against their unpadded slices,
                   library softmax with an explicit mask matrix
+  attn_fwd_decode Nq query rows against Nk keys, causal aligned bottom-right
+                  (FlashDecoding shapes, [P-wmrh] §5.1) -- a library softmax
+                  with an explicit mask, the square case of attn_fwd, the last
+                  rows of a square causal problem, Q = 0 and constant-V
+                  closed forms
   decode          binary16 / bfloat16 decoders -- all 65536 patterns vs a
                   library cast, hand-checked values
 """
@@ -108,6 +113,8 @@ def _bind(lib):
                                          p, i64, p, i64, p, p, p]
     lib.oracle_attn_fwd_masked.argtypes = [p, p, p, i32, i64, i64, i64, i64, i64, i64, p,
                                            f64, p, p]
+    lib.oracle_attn_fwd_decode.argtypes = [p, p, p, i32, i64, i64, i64, i64, i64, i32, f64,
+                                           p, p]
     lib.oracle_attn_bwd_masked.argtypes = [p, p, p, p, p, i32, i64, i64, i64, i64, i64, i64,
                                            p, f64, p, p, p]
     u64 = ctypes.c_uint64
@@ -126,7 +133,7 @@ def _bind(lib):
     for name in ("oracle_decode", "oracle_num_threads", "oracle_attn_fwd",
                  "oracle_attn_fwd_rows", "oracle_attn_probs", "oracle_attn_fwd_tiled",
                  "oracle_attn_bwd", "oracle_attn_bwd_rows", "oracle_attn_fwd_masked",
-                 "oracle_attn_bwd_masked",
+                 "oracle_attn_bwd_masked", "oracle_attn_fwd_decode",
                  "oracle_dropout_factors", "oracle_attn_fwd_dropout", "oracle_attn_bwd_dropout",
                  "oracle_attn_fwd_dropout_rows", "oracle_attn_bwd_dropout_rows"):
         getattr(lib, name).restype = ctypes.c_int
@@ -324,6 +331,25 @@ def _impl_attn_fwd_masked(lib, q, k, v, dtype, window_left: int, window_right: i
     return o, lse
 
 
+def _impl_attn_fwd_decode(lib, q, k, v, dtype, causal: bool, scale: float):
+    """Nq query rows (q: [B,H,Nq,d]) against Nk keys (k, v: [B,H,Nk,d]);
+    causal: query i uses keys j <= i + Nk - Nq.  Rows without keys: o = 0,
+    lse = -inf.  Returns (o [B,H,Nq,d], lse [B,H,Nq])."""
+    q, k, v = _bits(q), _bits(k), _bits(v)
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B,H,Nq,d]; k and v one [B,H,Nk,d] shape")
+    B, H, Nq, d = q.shape
+    if k.shape[:2] != (B, H) or k.shape[3] != d:
+        raise ValueError("q, k, v must share B, H and d")
+    Nk = k.shape[2]
+    o = np.empty((B, H, Nq, d), dtype=np.float64)
+    lse = np.empty((B, H, Nq), dtype=np.float64)
+    _check(lib.oracle_attn_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _dtype_code(dtype), B, H, Nq,
+                                      Nk, d, int(bool(causal)), float(scale), _ptr(o),
+                                      _ptr(lse)), "oracle_attn_fwd_decode")
+    return o, lse
+
+
 def _impl_attn_bwd_masked(lib, q, k, v, do, dtype, window_left: int, window_right: int,
                           seqlens, scale: float, o=None):
     """Gradients of attn_fwd_masked (same window and lengths) for upstream
@@ -500,7 +526,7 @@ def _impl_attn_bwd_dropout_rows(lib, q, k, v, do, o, dtype, causal: bool, scale:
 
 _API = ("num_threads", "decode", "softmax_1d", "softmax_online_1d", "attn_fwd",
         "attn_fwd_rows", "attn_probs", "attn_fwd_tiled", "attn_bwd", "attn_bwd_rows",
-        "attn_fwd_masked", "attn_bwd_masked", "philox4x32_10", "dropout_factors",
+        "attn_fwd_masked", "attn_bwd_masked", "attn_fwd_decode", "philox4x32_10", "dropout_factors",
         "attn_fwd_dropout", "attn_bwd_dropout", "attn_fwd_dropout_rows",
         "attn_bwd_dropout_rows")
 
@@ -543,6 +569,7 @@ attn_bwd = _module_fn("attn_bwd")
 attn_bwd_rows = _module_fn("attn_bwd_rows")
 attn_fwd_masked = _module_fn("attn_fwd_masked")
 attn_bwd_masked = _module_fn("attn_bwd_masked")
+attn_fwd_decode = _module_fn("attn_fwd_decode")
 philox4x32_10 = _module_fn("philox4x32_10")
 dropout_factors = _module_fn("dropout_factors")
 attn_fwd_dropout = _module_fn("attn_fwd_dropout")

@@ -707,6 +707,80 @@ int oracle_attn_fwd_masked(const uint16_t *q, const uint16_t *k, const uint16_t 
     return fail ? -2 : 0;
 }
 
+/* ---- queries against a longer run of keys (decoding) ---------------------
+ *
+ * "FlashAttention V2 核心原理与架构设计" (wmrh.cn) §5.1 pairs the kernel with
+ * FlashDecoding for sequences beyond 32K keys, where a few new query rows
+ * attend to a long cache of keys.  The page fixes no shapes; the reading
+ * used here: q and o are [B,H,Nq,d], k and v are [B,H,Nk,d].  Without the
+ * causal flag every query uses all Nk keys.  With it the queries are the
+ * last Nq positions of the sequence, so query i may use keys
+ * j <= i + (Nk - Nq) (bottom-right alignment; Nq = Nk is the square causal
+ * mask).  A query with no allowed key (possible only when Nq > Nk) gets
+ * o = 0 and lse = -inf. */
+int oracle_attn_fwd_decode(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                           int dtype, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                           int64_t d, int causal, double scale, double *o, double *lse)
+{
+    if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d < 1) return -1;
+    if (dtype != ORACLE_DTYPE_F16 && dtype != ORACLE_DTYPE_BF16) return -1;
+    const int64_t nq = B * H * Nq * d, nk = B * H * Nk * d;
+    double *qd = (double *)malloc((size_t)(nq > 0 ? nq : 1) * sizeof(double));
+    double *kd = (double *)malloc((size_t)(nk > 0 ? nk : 1) * sizeof(double));
+    double *vd = (double *)malloc((size_t)(nk > 0 ? nk : 1) * sizeof(double));
+    if (!qd || !kd || !vd) {
+        free(qd); free(kd); free(vd);
+        return -2;
+    }
+    decode_all(q, dtype, nq, qd);
+    decode_all(k, dtype, nk, kd);
+    decode_all(v, dtype, nk, vd);
+    const int64_t rows = B * H * Nq;
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc((size_t)(Nk > 0 ? Nk : 1) * sizeof(double));
+        if (!s) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t r = 0; r < rows; ++r) {
+                const int64_t bh = r / Nq, i = r % Nq;
+                int64_t hi = causal ? i + (Nk - Nq) : Nk - 1;   /* last allowed key */
+                if (hi > Nk - 1) hi = Nk - 1;
+                double *orow = o + r * d;
+                if (hi < 0) {
+                    for (int64_t c = 0; c < d; ++c) orow[c] = 0.0;
+                    lse[r] = -INFINITY;
+                    continue;
+                }
+                const double *qi = qd + r * d;
+                const double *kh = kd + bh * Nk * d, *vh = vd + bh * Nk * d;
+                double m = -INFINITY;
+                for (int64_t j = 0; j <= hi; ++j) {
+                    double dot = 0.0;
+                    for (int64_t c = 0; c < d; ++c) dot += qi[c] * kh[j * d + c];
+                    s[j] = scale * dot;
+                    if (s[j] > m) m = s[j];
+                }
+                double l = 0.0;
+                for (int64_t c = 0; c < d; ++c) orow[c] = 0.0;
+                for (int64_t j = 0; j <= hi; ++j) {
+                    const double wj = exp(s[j] - m);
+                    l += wj;
+                    for (int64_t c = 0; c < d; ++c) orow[c] += wj * vh[j * d + c];
+                }
+                for (int64_t c = 0; c < d; ++c) orow[c] /= l;
+                lse[r] = m + log(l);
+            }
+        }
+        free(s);
+    }
+    free(qd); free(kd); free(vd);
+    return fail ? -2 : 0;
+}
+
 /* Gradients of oracle_attn_fwd_masked for an upstream dO (same mask
  * reading): per row i with allowed keys lo..hi, P_ij = softmax of the
  * scores over those keys, dP_ij = dO_i . v_j, D_i = sum_j P_ij dP_ij (or

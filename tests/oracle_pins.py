@@ -499,6 +499,73 @@ def pin_dropout_rows(orc) -> bool:
     return ok
 
 
+# ---------------------------------------------------------------- decoding
+
+def decode_reference(q, k, v, causal: bool, scale: float):
+    """torch fp64 softmax over an explicit mask for Nq queries against Nk
+    keys: query i may use key j when j <= i + Nk - Nq if causal (every key
+    otherwise); rows without keys give o = 0 and lse = -inf."""
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    i = torch.arange(Nq)[:, None]
+    j = torch.arange(Nk)[None, :]
+    allow = (j <= i + (Nk - Nq)) if causal else torch.ones(Nq, Nk, dtype=torch.bool)
+    s = torch.matmul(q.double(), k.double().transpose(-1, -2).contiguous()) * scale
+    s = s.masked_fill(~allow, float("-inf"))
+    has = allow.any(-1)
+    o = np.zeros((B, H, Nq, d))
+    lse = np.full((B, H, Nq), -np.inf)
+    if bool(has.any()):
+        sh = s[:, :, has, :]
+        o[:, :, has.numpy()] = torch.matmul(torch.softmax(sh, dim=-1), v.double()).numpy()
+        lse[:, :, has.numpy()] = torch.logsumexp(sh, dim=-1).numpy()
+    return o, lse
+
+
+def _decode_qkv(B, H, Nq, Nk, d, dtype, seed):
+    q = make_qkv(B, H, Nq, d, dtype, seed=seed)[0]
+    _, k, v = make_qkv(B, H, Nk, d, dtype, seed=seed + 1)
+    return q, k, v
+
+
+def pin_decode(orc) -> bool:
+    ok = True
+    # a library softmax with the explicit bottom-right mask; B*H > 1 so the
+    # per-head strides of Q (Nq rows) and K/V (Nk rows) both matter
+    for dtype in ("f16", "bf16"):
+        for Nq, Nk in ((1, 37), (5, 37), (37, 37), (6, 4)):
+            q, k, v = _decode_qkv(2, 3, Nq, Nk, 8, dtype, seed=40 + Nq)
+            for causal in (False, True):
+                o, lse = orc.attn_fwd_decode(bits(q), bits(k), bits(v), dtype, causal, 0.35)
+                ro, rl = decode_reference(q, k, v, causal, 0.35)
+                fin = np.isfinite(rl)
+                ok &= bool(np.array_equal(fin, np.isfinite(lse)))
+                ok &= _close(o, ro, 1e-12) and _close(lse[fin], rl[fin], 1e-12)
+    # the last Nq rows of a square causal problem over the same keys
+    qf, k, v = _qkv(2, 2, 29, 8, "bf16", seed=47)
+    fo, fl = orc.attn_fwd(bits(qf), bits(k), bits(v), "bf16", True, 0.4)
+    for Nq in (1, 3, 29):
+        qs = qf[:, :, 29 - Nq:, :].contiguous()
+        o, lse = orc.attn_fwd_decode(bits(qs), bits(k), bits(v), "bf16", True, 0.4)
+        ok &= _close(o, fo[:, :, 29 - Nq:], 1e-15) and _close(lse, fl[:, :, 29 - Nq:], 1e-15)
+    # Q = 0: every allowed key weighs the same, so lse = ln |A_i| and o is
+    # the mean of the allowed V rows; constant V rows give that constant
+    Nq, Nk = 4, 11
+    q, k, v = _decode_qkv(1, 2, Nq, Nk, 8, "f16", seed=48)
+    z = torch.zeros_like(q)
+    vv = v.double().numpy()
+    for causal in (False, True):
+        o, lse = orc.attn_fwd_decode(bits(z), bits(k), bits(v), "f16", causal, 0.7)
+        for i in range(Nq):
+            n = (i + Nk - Nq + 1) if causal else Nk
+            ok &= _close(lse[:, :, i], np.full((1, 2), math.log(n)), 1e-15)
+            ok &= _close(o[:, :, i], vv[:, :, :n].mean(axis=2), 1e-14)
+        cv = torch.full_like(v, 1.625)
+        o, _ = orc.attn_fwd_decode(bits(q), bits(k), bits(cv), "f16", causal, 0.7)
+        ok &= _close(o, np.full(o.shape, 1.625), 1e-14)
+    return ok
+
+
 PINS = {
     "brute_force": pin_brute_force,
     "python_loops": pin_python_loops,
@@ -515,6 +582,7 @@ PINS = {
     "bwd_rows": pin_bwd_rows,
     "bwd_given_o": pin_bwd_given_o,
     "masked": pin_masked,
+    "decode": pin_decode,
     "bwd_masked": pin_bwd_masked,
     "philox_kat": pin_philox_kat,
     "dropout": pin_dropout,

@@ -18,7 +18,8 @@ import pytest
 import torch
 
 from io_aware_transformer_amd.inputs import bits, make_qkv, WORKLOADS
-from tests.oracle_pins import (PINS, _qkv, python_reference, run_pins, to_tensor,
+from tests.oracle_pins import (PINS, _decode_qkv, _qkv, decode_reference, pin_decode,
+                               python_reference, run_pins, to_tensor,
                                torch_reference)
 
 
@@ -422,6 +423,17 @@ MUTANTS = [
      "dropout fwd rows: wrong offset"),
     ("dvh[j * d + c] += prow[j] * z * doh[i * d + c];", "dvh[j * d + c] += prow[j] * doh[i * d + c];",
      "dropout bwd: dV without the keep factor"),
+    ("int64_t hi = causal ? i + (Nk - Nq) : Nk - 1;", "int64_t hi = causal ? i : Nk - 1;",
+     "decode: causal aligned top-left"),
+    ("int64_t hi = causal ? i + (Nk - Nq) : Nk - 1;", "int64_t hi = causal ? i + (Nk - Nq) + 1 : Nk - 1;",
+     "decode: causal diagonal off by one"),
+    ("const double *kh = kd + bh * Nk * d,", "const double *kh = kd + bh * Nq * d,",
+     "decode: K head stride of Q"),
+    ("                if (hi < 0) {\n                    for (int64_t c = 0; c < d; ++c) orow[c] = 0.0;",
+     "                if (hi < -1) {\n                    for (int64_t c = 0; c < d; ++c) orow[c] = 0.0;",
+     "decode: rows without keys not emptied"),
+    ("const double wj = exp(s[j] - m);", "const double wj = exp(m - s[j]);",
+     "decode: sign of the exponent"),
 ]
 
 
@@ -496,6 +508,32 @@ def test_bwd_uniform_weights_closed_form(oracle_mod):
 
 
 # ---------------------------------------------------------------- masks
+
+def test_decode_pin(oracle_mod):
+    assert pin_decode(oracle_mod)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(1, 1), (1, 300), (2, 129), (16, 1000), (64, 64), (70, 65)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_library(oracle_mod, Nq, Nk, causal):
+    """Decoding shapes against a library softmax with the explicit mask."""
+    for dtype in ("f16", "bf16"):
+        q, k, v = _decode_qkv(2, 2, Nq, Nk, 64, dtype, seed=Nq * 7 + Nk)
+        o, lse = oracle_mod.attn_fwd_decode(bits(q), bits(k), bits(v), dtype, causal, 0.125)
+        ro, rl = decode_reference(q, k, v, causal, 0.125)
+        fin = np.isfinite(rl)
+        assert np.array_equal(fin, np.isfinite(lse))
+        np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[fin], rl[fin], rtol=0, atol=1e-12)
+
+
+def test_decode_rejects_mismatched_shapes(oracle_mod):
+    q, k, v = _decode_qkv(1, 2, 3, 9, 8, "f16", seed=1)
+    with pytest.raises(ValueError):
+        oracle_mod.attn_fwd_decode(bits(q), bits(k), bits(v[:, :, :5]), "f16", False, 0.1)
+    with pytest.raises(ValueError):
+        oracle_mod.attn_fwd_decode(bits(q), bits(k[:, :1]), bits(v[:, :1]), "f16", False, 0.1)
+
 
 def test_masked_pin(oracle_mod):
     assert PINS["masked"](oracle_mod)
