@@ -11,7 +11,8 @@ to stderr.
                   [--extra n4k_full,n8k_full,n16k_d64]
                   [--backward n8k_causal_peaky] [--window n8k_causal_peaky:1023:0]
                   [--split n4k_h4_causal:4] [--dropout n8k_causal_peaky:0.1]
-                  [--varlen 32:128:8:512:8192] [--spinup 0.3]
+                  [--varlen 32:128:8:512:8192] [--decode 1:32:1:32768,1:32:16:131072]
+                  [--spinup 0.3]
                   [--no-cold] [--no-cpu-baseline] [--mode copy]
 
 The headline workload is B=1 H=32 N=8192 d=128 bf16 causal with Q,K x3;
@@ -24,7 +25,9 @@ ending at itself) under "window", and fa_fwd against fa_fwd_split on a few-head 
 the dropout forward and backward (fa_fwd_dropout, fa_bwd_dropout, p = 0.1) of the
 headline workload under "dropout", a causal bf16 forward and backward over 8
 packed sequences of seeded lengths in [512, 8192] (fa_fwd_varlen, fa_bwd_varlen,
-32 heads) under "varlen", and the headline forward with cold caches (a 512 MB
+32 heads) under "varlen", decoding shapes (fa_fwd_decode: a few query rows against
+32K or 128K keys, d128 bf16 causal, reported against the HBM peak since the
+keys and values are read once) under "decode", and the headline forward with cold caches (a 512 MB
 buffer overwritten before each launch) under "cold".  FLOP =
 4*B*H*N^2*d, halved when causal (backward: 2.5 times that).
 
@@ -341,6 +344,42 @@ def time_split(w, num_splits: int, steps: int, warmup: int, seed: int = 0):
     return out
 
 
+def time_decode(B: int, H: int, Nq: int, Nk: int, d: int, steps: int, warmup: int,
+                seed: int = 0):
+    """fa_fwd_decode (bf16, causal, the library's split count) of Nq query
+    rows against Nk keys: per-call HIP event time over both of its kernels
+    (mean of `steps` calls), the algorithmic HBM bytes and the FLOP."""
+    import torch
+    import io_aware_transformer_amd as fa
+    from io_aware_transformer_amd.inputs import make_qkv
+
+    dev = torch.device("cuda", 0)
+    q = make_qkv(B, H, Nq, d, "bf16", seed=seed)[0].to(dev)
+    _, k, v = (t.to(dev) for t in make_qkv(B, H, Nk, d, "bf16", seed=seed + 1))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    ns = fa.fa_fwd_decode_splits(B, H, Nq, Nk)
+    ws = torch.empty(fa.fa_fwd_decode_workspace_size(B, H, Nq, Nk, d, 0) // 4,
+                     dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    scale = d ** -0.5
+
+    def launch():
+        st = fa.fa_fwd_decode(q, k, v, o, lse, B, H, Nq, Nk, d, 1, scale, 0, ws,
+                              fa.FA_DTYPE_BF16, stream)
+        if st != fa.FA_OK:
+            raise fa.FaError(st)
+
+    spin(launch)
+    ms = event_times(launch, stream, steps, warmup)
+    # K and V read once, Q read and O written once, lse written
+    nbytes = B * H * (2 * Nk * d * 2 + 2 * Nq * d * 2 + Nq * 4)
+    # causal, bottom-right: query i uses i + Nk - Nq + 1 keys
+    keys = sum(i + Nk - Nq + 1 for i in range(Nq))
+    flop = 4 * B * H * d * keys
+    return {"ms_mean": sum(ms) / len(ms), "bytes": nbytes, "flop": flop, "num_splits": ns}
+
+
 def time_varlen(H: int, d: int, n_seq: int, lo: int, hi: int, steps: int, warmup: int):
     """fa_fwd_varlen (causal, bf16) on n_seq packed sequences of seeded
     lengths in [lo, hi], then fa_bwd_varlen on its (o, lse) and a seeded dO;
@@ -593,6 +632,10 @@ def main() -> int:
                          "('none' to skip)")
     ap.add_argument("--split", default="n4k_h4_causal:4",
                     help="WORKLOAD:SPLITS split-key forward reported beside ('none' to skip)")
+    ap.add_argument("--decode", default="1:32:1:32768,1:32:16:131072",
+                    help="comma-separated B:H:NQ:NK decoding shapes (d128 bf16 causal, "
+                         "fa_fwd_decode with the library's split count) reported beside "
+                         "('none' to skip)")
     ap.add_argument("--dropout", default="n8k_causal_peaky:0.1",
                     help="WORKLOAD:P dropout forward and backward reported beside "
                          "('none' to skip)")
@@ -761,6 +804,23 @@ def main() -> int:
                          "ms_fa_fwd_split": round(rs["fa_fwd_split"], 5),
                          "tflops_fa_fwd": round(tp, 2), "tflops_fa_fwd_split": round(ts, 2),
                          "frac_fa_fwd_split": round(ts / PEAK_BF16_TFLOPS, 4)}
+
+    if args.decode and args.decode != "none":
+        line["decode"] = []
+        for spec in args.decode.split(","):
+            dB, dH, dq, dk = (int(x) for x in spec.split(":"))
+            rd = time_decode(dB, dH, dq, dk, 128, args.steps, args.warmup)
+            gbs = rd["bytes"] / (rd["ms_mean"] * 1e-3) / 1e9
+            tfd = rd["flop"] / (rd["ms_mean"] * 1e-3) / 1e12
+            log(f"bench: decode B{dB} H{dH} Nq{dq} Nk{dk} d128 bf16 causal, "
+                f"{rd['num_splits']} splits: {rd['ms_mean']*1e3:.1f} us, {gbs:.0f} GB/s "
+                f"({100*gbs/PEAK_HBM_GBS:.1f}% of HBM peak), {tfd:.1f} TFLOP/s")
+            line["decode"].append({
+                "B": dB, "H": dH, "Nq": dq, "Nk": dk, "d": 128, "dtype": "bf16",
+                "causal": True, "num_splits": rd["num_splits"],
+                "ms_mean": round(rd["ms_mean"], 5), "bytes_per_step": rd["bytes"],
+                "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                "tflops": round(tfd, 2)})
 
     if args.varlen and args.varlen != "none":
         vh, vd, vn, vlo, vhi = (int(x) for x in args.varlen.split(":"))

@@ -153,6 +153,44 @@ fa_status fa_fwd_split(const void *q, const void *k, const void *v, void *o,
                        float scale, int num_splits, float *ws, fa_dtype dtype,
                        hipStream_t stream);
 
+/* Forward pass for decoding shapes: Nq query rows against Nk keys, the
+ * long-sequence case that "FlashAttention V2 核心原理与架构设计" (wmrh.cn)
+ * §5.1 hands to FlashDecoding (beyond 32K keys), computed as fa_fwd_split
+ * computes it: the keys are cut into segments of whole 128-key tiles that
+ * separate work-groups process, and a second kernel merges each row's
+ * segment results (lse = ln sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s).
+ *     o[b,h,i,:] = sum_j softmax_j(scale * q[b,h,i,:] . k[b,h,j,:]) v[b,h,j,:]
+ * over the allowed keys: all j < Nk, or, when causal, j <= i + Nk - Nq --
+ * the queries are the last Nq positions of the sequence (bottom-right
+ * alignment; Nq = Nk is fa_fwd's square causal mask).  The page fixes no
+ * shapes; this reading is the library's.
+ *   q, o        contiguous [B,H,Nq,d], one 16-bit type
+ *   k, v        contiguous [B,H,Nk,d], the same type
+ *   lse         contiguous fp32 [B,H,Nq]
+ *   Nq, Nk      1 .. FA_MAX_N; causal requires Nq <= Nk
+ *   num_splits  0 (let the library choose: fa_fwd_decode_splits) or
+ *               1 .. FA_MAX_SPLITS segments requested
+ *   ws          fa_fwd_decode_workspace_size(B, H, Nq, Nk, d, num_splits)
+ *               bytes of device scratch, 16-byte aligned
+ * Other arguments, ownership and errors as fa_fwd: FA_ERR_INVALID_ARG also
+ * for Nq > Nk when causal, num_splits out of range, a null ws or overlapping
+ * buffers; FA_ERR_UNSUPPORTED for Nq or Nk above FA_MAX_N; FA_ERR_MISALIGNED
+ * also for ws.  Two kernels are enqueued on `stream`. */
+fa_status fa_fwd_decode(const void *q, const void *k, const void *v, void *o,
+                        float *lse, int B, int H, int Nq, int Nk, int d,
+                        int causal, float scale, int num_splits, float *ws,
+                        fa_dtype dtype, hipStream_t stream);
+
+/* Bytes of ws that fa_fwd_decode needs: segments x B*H*Nq x (d + 1) fp32.
+ * 0 for arguments fa_fwd_decode would reject as sizes. */
+size_t fa_fwd_decode_workspace_size(int B, int H, int Nq, int Nk, int d,
+                                    int num_splits);
+
+/* The segment count fa_fwd_decode uses for num_splits = 0: about 256
+ * work-groups over the grid (one per compute unit), with at least 4 tiles of
+ * 128 keys per segment, at most FA_MAX_SPLITS.  0 for sizes below 1. */
+int fa_fwd_decode_splits(int B, int H, int Nq, int Nk);
+
 /* Size of the static per-device scratch of fa_fwd_split_noalloc. */
 #define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 

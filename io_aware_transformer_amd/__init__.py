@@ -16,6 +16,10 @@ C entry points mirrored here with the same names and argument order:
                dtype, stream) -> status
   fa_fwd_split_noalloc(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits,
                        dtype, stream) -> status
+  fa_fwd_decode(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, ws,
+                dtype, stream) -> status
+  fa_fwd_decode_workspace_size(B, H, Nq, Nk, d, num_splits) -> bytes
+  fa_fwd_decode_splits(B, H, Nq, Nk) -> segments
   fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, total, max_seqlen, d,
                 causal, scale, dtype, stream) -> status
   fa_fwd_split_workspace_size(B, H, N, d, num_splits) -> bytes
@@ -55,7 +59,8 @@ EXPORTED = ("fa_fwd_f16", "fa_fwd_bf16", "fa_fwd", "fa_fwd_window", "fa_fwd_spli
             "fa_fwd_split_workspace_size", "fa_status_string", "fa_bwd",
             "fa_bwd_workspace_size", "fa_fwd_dropout", "fa_bwd_dropout", "fa_fwd_varlen",
             "fa_bwd_varlen", "fa_bwd_varlen_workspace_size", "fa_bwd_window",
-            "fa_fwd_split_noalloc")
+            "fa_fwd_split_noalloc", "fa_fwd_decode", "fa_fwd_decode_workspace_size",
+            "fa_fwd_decode_splits")
 FA_MAX_SPLITS = 64
 FA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -98,6 +103,12 @@ def load():
     lib.fa_fwd_split_noalloc.argtypes = [p, p, p, p, p, i, i, i, i, i, f, i, i, p]
     lib.fa_fwd_split_noalloc.restype = ctypes.c_int
     lib.fa_fwd_split_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_fwd_decode.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, i, p, i, p]
+    lib.fa_fwd_decode.restype = ctypes.c_int
+    lib.fa_fwd_decode_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.fa_fwd_decode_workspace_size.restype = ctypes.c_size_t
+    lib.fa_fwd_decode_splits.argtypes = [i, i, i, i]
+    lib.fa_fwd_decode_splits.restype = ctypes.c_int
     lib.fa_fwd_split_workspace_size.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [p] * 10 + [i, i, i, i, i, f, i, p]
     lib.fa_bwd.restype = ctypes.c_int
@@ -172,6 +183,22 @@ def fa_fwd_split_noalloc(q, k, v, o, lse, B, H, N, d, causal, scale, num_splits,
     return load().fa_fwd_split_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B),
                                        int(H), int(N), int(d), int(causal), float(scale),
                                        int(num_splits), int(dtype), _stream(stream))
+
+
+def fa_fwd_decode(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, num_splits, ws, dtype,
+                  stream=None) -> int:
+    return load().fa_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                int(Nq), int(Nk), int(d), int(causal), float(scale),
+                                int(num_splits), _ptr(ws), int(dtype), _stream(stream))
+
+
+def fa_fwd_decode_workspace_size(B, H, Nq, Nk, d, num_splits) -> int:
+    return int(load().fa_fwd_decode_workspace_size(int(B), int(H), int(Nq), int(Nk), int(d),
+                                                   int(num_splits)))
+
+
+def fa_fwd_decode_splits(B, H, Nq, Nk) -> int:
+    return int(load().fa_fwd_decode_splits(int(B), int(H), int(Nq), int(Nk)))
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, H, total, max_seqlen, d, causal, scale,

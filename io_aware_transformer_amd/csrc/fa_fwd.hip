@@ -284,8 +284,8 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                    const u16 *__restrict__ V, u16 *__restrict__ O,
                    float *__restrict__ LSE, int BH, int N_in, int nqb, float c,
                    unsigned qand, unsigned qxor, int H, int wl, int wr,
-                   const int *__restrict__ LENS, int kseg, float *__restrict__ PO,
-                   float *__restrict__ PL, DropArgs dr)
+                   const int *__restrict__ LENS, int kseg, int nk_in,
+                   float *__restrict__ PO, float *__restrict__ PL, DropArgs dr)
 {
     static_assert(!DROP || MODE <= 1, "dropout is built for the full and causal masks");
     constexpr bool VARLEN = MODE >= 4;
@@ -344,13 +344,17 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         if (qblk * kBR >= N) return;                   // Q block past the sequence
     }
     const size_t head = row0 * D;
-    const int nbytes = N * T::kRowBytes;
+    // keys of the problem: mode 3 may run the rows against a separate key
+    // sequence of nk_in rows per head (decoding shapes); elsewhere the keys
+    // are the rows themselves
+    const int NKEYS = SPLIT ? nk_in : N;
+    const size_t khead = SPLIT ? (size_t)bh * (size_t)NKEYS * D : head;
     const __amdgpu_buffer_rsrc_t rq =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(Q + head), 0, nbytes, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(K + head), 0, nbytes, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(V + head), 0, nbytes, kRsrcWord3);
+        __builtin_amdgcn_make_buffer_rsrc((void *)(Q + head), 0, N * T::kRowBytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(K + khead), 0, NKEYS * T::kRowBytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(V + khead), 0, NKEYS * T::kRowBytes, kRsrcWord3);
 
     const int q0 = qblk * kBR + kRowsPerWave * w;   // first query row of this wave
     const int qrow = q0 + l32;                      // the query row of this lane
@@ -375,7 +379,8 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                                             : n_steps);
     // MODE 2: valid length of this batch element, the work-group's and this
     // wave's key ranges (in steps j_lo..j_hi), and the per-lane key bounds
-    int len = N, j_lo = 0, j_hi = -1, klo_row = 0, khi_row = -1, kbeg = 0, kend = N;
+    // len: valid rows (and keys, except in mode 3, where klen = NKEYS)
+    int len = N, klen = N, j_lo = 0, j_hi = -1, klo_row = 0, khi_row = -1, kbeg = 0, kend = N;
     // rows without keys: o = 0 / lse = -inf (or the fp32 partials in mode 3)
     const size_t prow = ((size_t)blockIdx.y * BH + bh) * N + qrow;
     auto write_empty = [&]() {
@@ -399,13 +404,14 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     };
     if constexpr (GEN) {
         len = LENS ? min(max(LENS[bh / H], 0), N) : N;
+        klen = SPLIT ? NKEYS : len;
         if constexpr (SPLIT) {
             kbeg = blockIdx.y * kseg;
-            kend = min(N, kbeg + kseg);
+            kend = min(klen, kbeg + kseg);
         }
         const int r0 = qblk * kBR, r1 = min(r0 + kBR, len) - 1;
         const int klo = max(wl < 0 ? 0 : max(0, r0 - wl), kbeg);
-        const int khi = min(wr < 0 ? len - 1 : min(len - 1, r1 + wr), kend - 1);
+        const int khi = min(wr < 0 ? klen - 1 : min(klen - 1, r1 + wr), kend - 1);
         if (r0 > r1 || klo > khi) {                    // no (row, key) pair in the work-group
             if (qrow < N) write_empty();
             return;
@@ -415,14 +421,14 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         if (q0 < len) {
             const int w1 = min(q0 + kRowsPerWave, len) - 1;
             const int wlo = max(wl < 0 ? 0 : max(0, q0 - wl), kbeg);
-            const int whi = min(wr < 0 ? len - 1 : min(len - 1, w1 + wr), kend - 1);
+            const int whi = min(wr < 0 ? klen - 1 : min(klen - 1, w1 + wr), kend - 1);
             if (wlo <= whi) {
                 j_lo = wlo / kBC;
                 j_hi = whi / kBC;
             }
         }
         klo_row = max(wl < 0 ? 0 : qrow - wl, kbeg);
-        khi_row = min(wr < 0 ? len - 1 : min(len - 1, qrow + wr), kend - 1);
+        khi_row = min(wr < 0 ? klen - 1 : min(klen - 1, qrow + wr), kend - 1);
     }
 
     // ---- HBM -> LDS tile loads (each wave moves its share, 1 KB per load)
@@ -671,7 +677,7 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             const int w1 = q0 + kRowsPerWave - 1;
             const bool lo_ok = t * kBC >= max(wl < 0 ? 0 : w1 - wl, kbeg);
             const bool hi_ok = t * kBC + kBC - 1 <=
-                               min(wr < 0 ? len - 1 : min(len - 1, q0 + wr), kend - 1);
+                               min(wr < 0 ? klen - 1 : min(klen - 1, q0 + wr), kend - 1);
             mk = !(lo_ok && hi_ok);
         } else {
             mk = (CAUSAL && t * kBC + kBC - 1 > q0) || (t * kBC + kBC > N);
@@ -788,7 +794,7 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
 typedef void (*kernel_fn)(const u16 *, const u16 *, const u16 *, u16 *, float *,
                           int, int, int, float, unsigned, unsigned, int, int, int,
-                          const int *, int, float *, float *, DropArgs);
+                          const int *, int, int, float *, float *, DropArgs);
 
 template <int DT, int D>
 kernel_fn pick_d(int mode, bool drop)
@@ -896,9 +902,11 @@ fa_status launch_fwd(const void *q, const void *k, const void *v, void *o, float
                      int H, int N, int d, int mode, int wl, int wr, const int *lens,
                      float scale, fa_dtype dtype, hipStream_t stream, int nseg = 1,
                      int kseg = 0, float *po = nullptr, float *pl = nullptr,
-                     const DropArgs *drop = nullptr, int max_rows = 0)
+                     const DropArgs *drop = nullptr, int max_rows = 0, int nk = 0)
 {
-    if (mode < 4) {
+    // nk > 0 (mode 3 only): the rows run against nk keys per head, and the
+    // caller has validated the differently sized tensors itself
+    if (mode < 4 && nk == 0) {
         const fa_status vs = validate_fwd(q, k, v, o, lse, B, H, N, d, lens, scale, dtype);
         if (vs != FA_OK) return vs;
     }
@@ -916,14 +924,14 @@ fa_status launch_fwd(const void *q, const void *k, const void *v, void *o, float
     unsigned qand = (scale == 0.f) ? 0u : 0xffffffffu;
     unsigned qxor = (scale < 0.f) ? 0x80008000u : 0u;
     int bh_i = (int)BH, n_i = N, nqb_i = (int)nqb, h_i = H, wl_i = wl, wr_i = wr;
-    int kseg_i = kseg;
+    int kseg_i = kseg, nk_i = nk > 0 ? nk : N;
     const void *qp = q, *kp = k, *vp = v;
     void *op = o;
     float *lp = lse, *pop = po, *plp = pl;
     const int *lensp = lens;
     DropArgs dr = drop ? *drop : DropArgs{0u, 0u, 0u, 256u, 1.f};
     void *args[] = {&qp, &kp, &vp, &op, &lp, &bh_i, &n_i, &nqb_i, &c, &qand, &qxor,
-                    &h_i, &wl_i, &wr_i, &lensp, &kseg_i, &pop, &plp, &dr};
+                    &h_i, &wl_i, &wr_i, &lensp, &kseg_i, &nk_i, &pop, &plp, &dr};
     hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)grid, (unsigned)nseg),
                                    dim3(kThreads), args, 0, stream);
     if (e != hipSuccess) return FA_ERR_LAUNCH;
@@ -1022,6 +1030,77 @@ extern "C" fa_status fa_fwd_split(const void *q, const void *k, const void *v, v
     float *pl = ws + (size_t)nseg * B * H * N * d;
     return launch_fwd(q, k, v, o, lse, B, H, N, d, 3, -1, causal ? 0 : -1, nullptr, scale,
                       dtype, stream, nseg, kseg, po, pl);
+}
+
+// Key segments for fa_fwd_decode's num_splits = 0: enough that the grid
+// holds about one work-group per compute unit (256; a work-group takes most
+// of a CU's LDS), with at least kMinSegTiles LDS tiles of keys per segment.
+static constexpr int kMinSegTiles = 4;
+static int decode_splits(int B, int H, int Nq, int Nk)
+{
+    const long long wg = (long long)B * H * ((Nq + kBR - 1) / kBR);
+    long long ns = (256 + wg - 1) / wg;
+    const long long by_keys = Nk / (kMinSegTiles * kLT);
+    if (ns > by_keys) ns = by_keys;
+    if (ns > FA_MAX_SPLITS) ns = FA_MAX_SPLITS;
+    return ns < 1 ? 1 : (int)ns;
+}
+
+extern "C" int fa_fwd_decode_splits(int B, int H, int Nq, int Nk)
+{
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return 0;
+    return decode_splits(B, H, Nq, Nk);
+}
+
+extern "C" size_t fa_fwd_decode_workspace_size(int B, int H, int Nq, int Nk, int d,
+                                               int num_splits)
+{
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (d != 64 && d != 128) || num_splits < 0 ||
+        num_splits > FA_MAX_SPLITS)
+        return 0;
+    const int ns = num_splits ? num_splits : decode_splits(B, H, Nq, Nk);
+    const int kseg = split_kseg(Nk, ns);
+    const size_t nseg = (size_t)((Nk + kseg - 1) / kseg);
+    return nseg * (size_t)B * (size_t)H * (size_t)Nq * (size_t)(d + 1) * sizeof(float);
+}
+
+extern "C" fa_status fa_fwd_decode(const void *q, const void *k, const void *v, void *o,
+                                   float *lse, int B, int H, int Nq, int Nk, int d, int causal,
+                                   float scale, int num_splits, float *ws, fa_dtype dtype,
+                                   hipStream_t stream)
+{
+    if (!q || !k || !v || !o || !lse || !ws) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (causal && Nq > Nk) return FA_ERR_INVALID_ARG;
+    if (num_splits < 0 || num_splits > FA_MAX_SPLITS) return FA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (Nq > FA_MAX_N || Nk > FA_MAX_N) return FA_ERR_UNSUPPORTED;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)ws) & 15)
+        return FA_ERR_MISALIGNED;
+    if ((uintptr_t)lse & 3) return FA_ERR_MISALIGNED;
+    const long long BH = (long long)B * H;
+    const long long grid = BH * ((Nq + kBR - 1) / kBR);
+    if (BH > INT_MAX || grid > INT_MAX) return FA_ERR_INVALID_ARG;
+    const size_t qb = (size_t)BH * Nq * d * 2, kb = (size_t)BH * Nk * d * 2;
+    const size_t lb = (size_t)BH * Nq * 4;
+    const size_t wsb = fa_fwd_decode_workspace_size(B, H, Nq, Nk, d, num_splits);
+    if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kb) || overlaps(o, qb, v, kb) ||
+        overlaps(lse, lb, q, qb) || overlaps(lse, lb, k, kb) || overlaps(lse, lb, v, kb) ||
+        overlaps(lse, lb, o, qb) || overlaps(ws, wsb, q, qb) || overlaps(ws, wsb, k, kb) ||
+        overlaps(ws, wsb, v, kb) || overlaps(ws, wsb, o, qb) || overlaps(ws, wsb, lse, lb))
+        return FA_ERR_INVALID_ARG;
+    const int ns = num_splits ? num_splits : decode_splits(B, H, Nq, Nk);
+    const int kseg = split_kseg(Nk, ns);
+    const int nseg = (Nk + kseg - 1) / kseg;
+    float *po = ws;
+    float *pl = ws + (size_t)nseg * BH * Nq * d;
+    // causal: the queries are the last Nq positions, so query i may use keys
+    // up to i + Nk - Nq (a window right side of Nk - Nq >= 0)
+    return launch_fwd(q, k, v, o, lse, B, H, Nq, d, 3, -1, causal ? Nk - Nq : -1, nullptr,
+                      scale, dtype, stream, nseg, kseg, po, pl, nullptr, 0, Nk);
 }
 
 // Split partials of fa_fwd_split_noalloc: each device holds its own copy.

@@ -250,6 +250,53 @@ def test_split_noalloc_unsupported_misaligned_and_too_large():
     assert ncall(N=n_fit + 1, ns=1, **far) == fa.FA_ERR_SCRATCH
 
 
+# ---------------------------------------------------------------- decoding
+
+QD, KD, VD, OD, LD, WD = ((1 << 36) * (i + 1) for i in range(6))
+
+
+def dccall(q=QD, k=KD, v=VD, o=OD, lse=LD, B=1, H=2, Nq=4, Nk=1000, d=128, causal=1,
+           scale=0.125, ns=0, ws=WD, dtype=fa.FA_DTYPE_BF16):
+    return fa.fa_fwd_decode(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, ns, ws, dtype, None)
+
+
+def test_decode_workspace_size_and_split_rule():
+    # segments of whole 128-key tiles: Nk = 1000 in 3 splits -> 384 + 384 + 232
+    assert fa.fa_fwd_decode_workspace_size(1, 2, 4, 1000, 128, 3) == 3 * 2 * 4 * 129 * 4
+    assert fa.fa_fwd_decode_workspace_size(2, 3, 5, 100, 64, 64) == 1 * 6 * 5 * 65 * 4
+    # num_splits = 0 resolves to the library's rule
+    ns = fa.fa_fwd_decode_splits(1, 32, 1, 32768)
+    assert ns == 8      # 32 work-groups -> 8 segments of 4096 keys: 256 work-groups
+    assert fa.fa_fwd_decode_workspace_size(1, 32, 1, 32768, 128, 0) == 8 * 32 * 1 * 129 * 4
+    assert fa.fa_fwd_decode_splits(1, 1, 1, 1 << 22) == fa.FA_MAX_SPLITS
+    assert fa.fa_fwd_decode_splits(1, 1, 1, 300) == 1        # under 4 tiles per segment
+    assert fa.fa_fwd_decode_splits(1, 4, 300, 65536) == 32   # 8 work-groups
+    assert fa.fa_fwd_decode_splits(64, 32, 1, 65536) == 1
+    assert fa.fa_fwd_decode_splits(0, 1, 1, 1) == 0
+    for bad in ((0, 1, 1, 1, 64, 1), (1, 1, 0, 1, 64, 1), (1, 1, 1, 0, 64, 1),
+                (1, 1, 1, 1, 96, 1), (1, 1, 1, 1, 64, -1), (1, 1, 1, 1, 64, 65)):
+        assert fa.fa_fwd_decode_workspace_size(*bad) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(q=0), dict(k=0), dict(v=0), dict(o=0), dict(lse=0),
+                                dict(ws=0), dict(B=0), dict(H=0), dict(Nq=0), dict(Nk=0),
+                                dict(causal=2), dict(Nq=1001), dict(ns=-1), dict(ns=65),
+                                dict(scale=float("inf")), dict(dtype=2), dict(o=QD),
+                                dict(lse=KD + 64), dict(ws=OD), dict(o=KD + 1024)])
+def test_decode_invalid(kw):
+    assert dccall(**kw) == fa.FA_ERR_INVALID_ARG
+
+
+def test_decode_unsupported_and_misaligned():
+    assert dccall(d=32) == fa.FA_ERR_UNSUPPORTED
+    assert dccall(Nk=(1 << 22) + 1) == fa.FA_ERR_UNSUPPORTED
+    assert dccall(Nq=(1 << 22) + 1, causal=0) == fa.FA_ERR_UNSUPPORTED
+    for kw in (dict(q=QD + 8), dict(k=KD + 2), dict(ws=WD + 4), dict(lse=LD + 2)):
+        assert dccall(**kw) == fa.FA_ERR_MISALIGNED
+    # non-causal decoding allows more queries than keys
+    assert fa.fa_fwd_decode_workspace_size(1, 1, 50, 10, 64, 1) > 0
+
+
 # ---------------------------------------------------------------- dropout
 
 def dcall(q=Q, k=K, v=V, o=O, lse=L, B=1, H=1, N=64, d=128, causal=0, scale=0.125, p=0.1,

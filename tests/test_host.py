@@ -77,7 +77,8 @@ def test_bench_help_names_every_option():
     r = _bench("--help")
     assert r.returncode == 0
     for opt in ("--gpus", "--steps", "--warmup", "--workload", "--secondary", "--extra",
-                "--backward", "--window", "--split", "--dropout", "--varlen", "--spinup",
+                "--backward", "--window", "--split", "--dropout", "--varlen", "--decode",
+                "--spinup",
                 "--no-cold", "--no-cpu-baseline"):
         assert opt in r.stdout, opt
 
