@@ -774,21 +774,53 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         // undropped fp32 row sum; otherwise over the rounded-weight sum
         const float lht = DROP ? 0.f : half_sum(lh);
         const float lt = FSUM ? half_sum(l) : lht;
-        if (GEN ? (qrow < len) : (qrow < N)) {
-            const float inv = DROP ? dr.fscale / lt : 1.f / lht;
-            u16 *orow = O + head + (size_t)qrow * D;
+        const float inv = DROP ? dr.fscale / lt : 1.f / lht;
+        // O leaves through this wave's own 32-row slice of the idle K
+        // buffers (the loop's last barrier has retired every tile read and
+        // load): a lane holds 4 consecutive columns of its row per (db, g),
+        // i.e. half of 16-byte chunk 4*db + g of that row.  Read back as whole
+        // chunks, one store instruction writes 64 * 16 / (2 * D) complete
+        // consecutive rows, a contiguous run of the head's row-major O.
+        // Chunks are XOR-swizzled by row so each LDS access spreads over the
+        // banks.
+        constexpr int CH = T::kChunks;                    // 16-byte chunks per row
+        LDS unsigned char *stage = (w < kWaves / 2 ? bufp(Buf<0>{}) : bufp(Buf<1>{})) +
+                                   (w % (kWaves / 2)) * (kRowsPerWave * T::kRowBytes);
+        static_assert((kWaves / 2) * kRowsPerWave * T::kRowBytes <= T::kBytes,
+                      "four O slices fit one K buffer");
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    u32x2 pr;
-                    pr[0] = E::pack2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
-                    pr[1] = E::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-                    *(u32x2 *)(orow + 32 * db + 8 * g + 4 * hh) = pr;
-                }
-            if (hh == 0)
-                LSE[row0 + qrow] = (m + log2f(lt)) * 0.69314718055994530942f;
+            for (int g = 0; g < 4; ++g) {
+                u32x2 pr;
+                pr[0] = E::pack2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
+                pr[1] = E::pack2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+                const int c = 4 * db + g;
+                *(LDS u32x2 *)(stage + l32 * T::kRowBytes + ((c ^ (l32 & (CH - 1))) << 4) +
+                               8 * hh) = pr;
+            }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        constexpr int RPI = 64 / CH;                      // rows per store instruction
+        constexpr int NIT = kRowsPerWave / RPI;
+        const int rr = lane / CH, cc = lane % CH;
+        u32x4 x[NIT];                                     // all reads first, then the stores
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int r = it * RPI + rr;
+            x[it] = *(const LDS u32x4 *)(stage + r * T::kRowBytes + ((cc ^ (r & (CH - 1))) << 4));
         }
+        const int rows_ok = (GEN ? len : N) - q0;         // valid rows of this wave's slab
+        u16 *obase = O + head + (size_t)q0 * D + 8 * cc;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int r = it * RPI + rr;
+            if (rows_ok >= kRowsPerWave || r < rows_ok)
+                *(u32x4 *)(obase + (size_t)r * D) = x[it];
+        }
+        if ((GEN ? (qrow < len) : (qrow < N)) && hh == 0)
+            LSE[row0 + qrow] = (m + log2f(lt)) * 0.69314718055994530942f;
     }
 }
 
