@@ -12,6 +12,13 @@ ROOT = PKG.parent
 SOURCES = [PKG / "csrc" / "fa_fwd.hip", PKG / "csrc" / "fa_bwd.hip"]
 HEADERS = [ROOT / "include" / "fa_fwd.h", ROOT / "include" / "fa_bwd.h"]
 LIB = PKG / "libfa_fwd.so"
+# Race-check builds of the forward source (not the product): LDS poisoned
+# with NaN patterns at kernel start, and tile loads serialised behind the
+# reads; both must reproduce the product's outputs bit for bit.
+DEBUG_LIBS = {
+    "poison": (PKG / "libfa_fwd_debug_poison.so", ["-DFA_DEBUG_LDS_POISON"]),
+    "serial": (PKG / "libfa_fwd_debug_serial.so", ["-DFA_DEBUG_SERIAL_TILES"]),
+}
 
 HIPCC_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
@@ -39,5 +46,21 @@ def build(verbose: bool = False) -> Path:
     return LIB
 
 
+def build_debug(verbose: bool = False) -> list:
+    """Compile the race-check builds of the forward source (always recompiles)."""
+    out = []
+    for path, defs in DEBUG_LIBS.values():
+        tmp = path.with_suffix(".so.tmp")
+        cmd = [hipcc(), *HIPCC_FLAGS, *defs, f"-I{ROOT / 'include'}", str(SOURCES[0]), "-o",
+               str(tmp)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, path)
+        out.append(path)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_debug(verbose=True))

@@ -317,6 +317,28 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
+#ifdef FA_DEBUG_LDS_POISON
+    // Race-check build: every LDS byte starts as an all-ones (NaN) pattern,
+    // so an operand read that overtook its tile load, or a tile read after
+    // its buffer was refilled, turns the outputs into NaN or changes them.
+    {
+        const u32x4 nan4 = {~0u, ~0u, ~0u, ~0u};
+        for (int i = tid; i < T::kBytes / 16; i += kThreads) {
+            ((LDS u32x4 *)k0s)[i] = nan4;
+            ((LDS u32x4 *)k1s)[i] = nan4;
+            ((LDS u32x4 *)v0s)[i] = nan4;
+            ((LDS u32x4 *)v1s)[i] = nan4;
+        }
+        __syncthreads();
+    }
+#endif
+#ifdef FA_DEBUG_SERIAL_TILES
+    // Race-check build: tile t+1 is loaded only after tile t is done
+    // (loads, wait, barrier), so no load overlaps any read
+    constexpr bool kSerial = true;
+#else
+    constexpr bool kSerial = false;
+#endif
     // wave index (kRowsPerWave query rows each).  At d = 128 it is held in a
     // scalar register, so tile-load addressing stays on the scalar unit (at
     // d = 64 that measured no faster)
@@ -712,7 +734,7 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                 sub = u;
                 u32x4 pk[PT];
                 __builtin_amdgcn_s_setprio(2);
-                if (u == 0) qk(sc, Buf<P>{}, Flag<true>{}, Buf<1 - P>{}, Buf<3 - P>{}, base);
+                if (u == 0) qk(sc, Buf<P>{}, Flag<!kSerial>{}, Buf<1 - P>{}, Buf<3 - P>{}, base);
                 else qk(sc, Buf<P>{}, Flag<false>{}, Buf<1 - P>{}, Buf<3 - P>{}, base);
                 __builtin_amdgcn_s_setprio(0);
                 if (tile_masked(j)) mask(sc, j);
@@ -723,7 +745,7 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                 pv(Buf<2 + P>{}, pk);
                 __builtin_amdgcn_s_setprio(0);
                 __builtin_amdgcn_sched_barrier(0);
-            } else if (u == 0) {
+            } else if (u == 0 && !kSerial) {
 #pragma unroll
                 for (int n = 0; n < 2 * T::kLoadsPerWave; ++n)
                     issue_one(n, Buf<1 - P>{}, Buf<3 - P>{}, base);
@@ -731,6 +753,13 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if constexpr (kSerial) {
+#pragma unroll
+            for (int n = 0; n < 2 * T::kLoadsPerWave; ++n)
+                issue_one(n, Buf<1 - P>{}, Buf<3 - P>{}, base);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
     };
 
     for (int t = t_begin; t < n_tiles; t += 2) {
