@@ -10,7 +10,7 @@ to stderr.
                   [--workload n8k_causal_peaky] [--secondary n4k_causal]
                   [--extra n4k_full,n8k_full,n16k_d64]
                   [--backward n8k_causal_peaky] [--window n8k_causal_peaky:1023:0]
-                  [--split n4k_h4_causal:4] [--dropout n8k_causal_peaky:0.1]
+                  [--split n4k_h4_causal:4,n16k_d64:2] [--dropout n8k_causal_peaky:0.1]
                   [--varlen 32:128:8:512:8192] [--decode 1:32:1:32768,1:32:16:131072]
                   [--spinup 0.3]
                   [--no-cold] [--no-cpu-baseline] [--mode copy]
@@ -21,7 +21,8 @@ B=2 H=16 N=4096 and B=1 H=32 N=8192 d=128 bf16 forwards and the few-head
 B=1 H=4 N=16384 d=64 fp16 forward under "extra", and the backward
 pass (fa_bwd) of the headline workload under "backward", and a sliding-window
 forward and backward (fa_fwd_window, fa_bwd_window; each query sees the 1024 keys
-ending at itself) under "window", and fa_fwd against fa_fwd_split on a few-head shape under "split", and
+ending at itself) under "window", and fa_fwd against fa_fwd_split on two few-head shapes (B=1 H=4 N=4096 d=128 causal,
+and the N=16384 d=64 one) under "split", and
 the dropout forward and backward (fa_fwd_dropout, fa_bwd_dropout, p = 0.1) of the
 headline workload under "dropout", a causal bf16 forward and backward over 8
 packed sequences of seeded lengths in [512, 8192] (fa_fwd_varlen, fa_bwd_varlen,
@@ -630,8 +631,9 @@ def main() -> int:
     ap.add_argument("--window", default="n8k_causal_peaky:1023:0",
                     help="WORKLOAD:LEFT:RIGHT sliding-window forward reported beside "
                          "('none' to skip)")
-    ap.add_argument("--split", default="n4k_h4_causal:4",
-                    help="WORKLOAD:SPLITS split-key forward reported beside ('none' to skip)")
+    ap.add_argument("--split", default="n4k_h4_causal:4,n16k_d64:2",
+                    help="comma-separated WORKLOAD:SPLITS split-key forwards reported beside "
+                         "('none' to skip)")
     ap.add_argument("--decode", default="1:32:1:32768,1:32:16:131072",
                     help="comma-separated B:H:NQ:NK decoding shapes (d128 bf16 causal, "
                          "fa_fwd_decode with the library's split count) reported beside "
@@ -791,19 +793,23 @@ def main() -> int:
                           "bwd_frac": round(twb / PEAK_BF16_TFLOPS, 4)}
 
     if args.split and args.split != "none":
-        sname, ns = args.split.split(":")
-        wsp = WORKLOADS[sname]
-        rs = time_split(wsp, int(ns), args.steps, args.warmup)
-        ts = wsp.flops / (rs["fa_fwd_split"] * 1e-3) / 1e12
-        tp = wsp.flops / (rs["fa_fwd"] * 1e-3) / 1e12
-        log(f"bench: split {sname} x{ns}: fa_fwd {rs['fa_fwd']*1e3:.1f} us ({tp:.1f} TFLOP/s), "
-            f"fa_fwd_split {rs['fa_fwd_split']*1e3:.1f} us ({ts:.1f} TFLOP/s)")
-        line["split"] = {"workload": wsp.name, "B": wsp.B, "H": wsp.H, "N": wsp.N, "d": wsp.d,
-                         "causal": wsp.causal, "num_splits": int(ns),
-                         "ms_fa_fwd": round(rs["fa_fwd"], 5),
-                         "ms_fa_fwd_split": round(rs["fa_fwd_split"], 5),
-                         "tflops_fa_fwd": round(tp, 2), "tflops_fa_fwd_split": round(ts, 2),
-                         "frac_fa_fwd_split": round(ts / PEAK_BF16_TFLOPS, 4)}
+        line["split"] = []
+        for spec in args.split.split(","):
+            sname, ns = spec.split(":")
+            wsp = WORKLOADS[sname]
+            rs = time_split(wsp, int(ns), args.steps, args.warmup)
+            ts = wsp.flops / (rs["fa_fwd_split"] * 1e-3) / 1e12
+            tp = wsp.flops / (rs["fa_fwd"] * 1e-3) / 1e12
+            log(f"bench: split {sname} x{ns}: fa_fwd {rs['fa_fwd']*1e3:.1f} us "
+                f"({tp:.1f} TFLOP/s), fa_fwd_split {rs['fa_fwd_split']*1e3:.1f} us "
+                f"({ts:.1f} TFLOP/s)")
+            line["split"].append({
+                "workload": wsp.name, "B": wsp.B, "H": wsp.H, "N": wsp.N, "d": wsp.d,
+                "causal": wsp.causal, "num_splits": int(ns),
+                "ms_fa_fwd": round(rs["fa_fwd"], 5), "ms_fa_fwd_split": round(rs["fa_fwd_split"], 5),
+                "tflops_fa_fwd": round(tp, 2), "tflops_fa_fwd_split": round(ts, 2),
+                "frac_fa_fwd": round(tp / PEAK_BF16_TFLOPS, 4),
+                "frac_fa_fwd_split": round(ts / PEAK_BF16_TFLOPS, 4)})
 
     if args.decode and args.decode != "none":
         line["decode"] = []

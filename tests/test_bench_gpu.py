@@ -38,7 +38,8 @@ def test_bench_json_line():
     assert rf["traffic"] is None or rf["traffic"] > 0
     cb = j["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
-    for rec in ("secondary", "backward", "window", "split", "dropout", "varlen", "cold"):
+    for rec in ("secondary", "backward", "window", "split", "dropout", "varlen", "decode",
+                "cold"):
         assert rec in j, rec
     assert [e["workload"] for e in j["extra"]] == ["n4k_full", "n8k_full", "n16k_d64"]
     for e in j["extra"]:
