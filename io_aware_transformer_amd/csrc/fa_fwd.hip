@@ -881,6 +881,8 @@ kernel_fn pick(int d, int mode, bool drop)
 // split-K/V combination of "FlashAttention V2 核心原理与架构设计" §5.1):
 // lse = ln sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s, O rounded once.
 // D / 4 lanes per row, 4 elements each.
+constexpr int kMergeBatch = 16;   // segments whose loads the merge issues together
+
 template <int DT, int D>
 __global__ __launch_bounds__(256)
 void fa_fwd_merge_kernel(const float *__restrict__ PO, const float *__restrict__ PL,
@@ -893,19 +895,45 @@ void fa_fwd_merge_kernel(const float *__restrict__ PO, const float *__restrict__
     const long long r = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
     const int part = threadIdx.x % LPR;
     if (r >= rows) return;
-    float mx = neg_inf();
-    for (int s = 0; s < nseg; ++s) mx = fmaxf(mx, PL[(size_t)s * rows + r]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float sum = 0.f;
-    if (mx != neg_inf()) {
-        for (int s = 0; s < nseg; ++s) {
-            const float ls = PL[(size_t)s * rows + r];
-            if (ls == neg_inf()) continue;
-            const float wgt = __expf(ls - mx);
-            sum += wgt;
-            const f32x4 x = *(const f32x4 *)(PO + ((size_t)s * rows + r) * D + 4 * part);
+    float sum = 0.f, mx = neg_inf();
+    if (nseg <= kMergeBatch) {
+        // every segment's lse and O slice requested at once, then combined
+        float ls[kMergeBatch];
+        f32x4 x[kMergeBatch];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, x[e], acc[e]);
+        for (int s = 0; s < kMergeBatch; ++s) {
+            if (s < nseg) {
+                ls[s] = PL[(size_t)s * rows + r];
+                x[s] = *(const f32x4 *)(PO + ((size_t)s * rows + r) * D + 4 * part);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < kMergeBatch; ++s)
+            if (s < nseg) mx = fmaxf(mx, ls[s]);
+        if (mx != neg_inf()) {
+#pragma unroll
+            for (int s = 0; s < kMergeBatch; ++s) {
+                if (s < nseg && ls[s] != neg_inf()) {
+                    const float wgt = __expf(ls[s] - mx);
+                    sum += wgt;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, x[s][e], acc[e]);
+                }
+            }
+        }
+    } else {
+        for (int s = 0; s < nseg; ++s) mx = fmaxf(mx, PL[(size_t)s * rows + r]);
+        if (mx != neg_inf()) {
+            for (int s = 0; s < nseg; ++s) {
+                const float ls = PL[(size_t)s * rows + r];
+                if (ls == neg_inf()) continue;
+                const float wgt = __expf(ls - mx);
+                sum += wgt;
+                const f32x4 x = *(const f32x4 *)(PO + ((size_t)s * rows + r) * D + 4 * part);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, x[e], acc[e]);
+            }
         }
     }
     const float inv = sum > 0.f ? 1.f / sum : 0.f;
