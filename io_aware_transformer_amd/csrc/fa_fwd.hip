@@ -103,6 +103,15 @@ constexpr int kBC = 64;                          // keys per compute step
 constexpr int kLT = 128;                         // keys per LDS tile
 constexpr int kNSub = kLT / kBC;                 // compute steps per LDS tile
 constexpr float kLazy = 8.0f;                    // reference-max slack, log2 units
+// For binary16 the reference is kept kF16Lift (log2 units) below the running
+// row maximum: the weights are lifted by 2^kF16Lift, the largest then being
+// 2^(kLazy + kF16Lift) = 2^15 < 65504, and a weight 2^-31 below the row
+// maximum still rounds to a nonzero binary16.  Against the maximum itself,
+// everything under 2^-25 would round to 0: a flat tail of 2^20 keys each 18
+// nats under a dominant key (about 1.6% of the row) would vanish.  The lift
+// cancels in O (numerator and row sums carry it alike) and in lse (which is
+// the reference plus the log of the lifted sum).
+constexpr float kF16Lift = 7.0f;
 constexpr int kQkAhead = 4;                      // K operand reads in flight (MFMAs)
 constexpr int kPvAhead = 3;                      // V operand reads in flight (MFMAs)
 constexpr unsigned kRsrcWord3 = 0x00020000u;     // raw buffer, 32-bit data
@@ -578,7 +587,7 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
             }
     };
 
-    float m = neg_inf();   // reference max, log2 domain
+    float m = neg_inf();   // reference max, log2 domain (kF16Lift below the maximum for binary16)
     float l = 0.f;         // this lane's half of the row sum of P (fp32)
     float lh = 0.f;        // the same sum of P rounded to 16 bits
     f32x16 oacc[DB];
@@ -594,8 +603,9 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         for (int i = 0; i < NKB * 16; ++i) v[i] = s[i >> 4][i & 15];
         const float mx = TreeMax<NKB * 16>::of(v);
         const float mt = half_max(mx) * c;
-        if (__builtin_amdgcn_ballot_w64(mt > m + kLazy)) {
-            const float mn = fmaxf(m, mt);
+        constexpr float lift = (DT == FA_DTYPE_F16) ? kF16Lift : 0.f;
+        if (__builtin_amdgcn_ballot_w64(mt > m + (kLazy + lift))) {
+            const float mn = fmaxf(m, mt - lift);
             const float mu = (mn == neg_inf()) ? 0.f : mn;
             const float alpha = __builtin_amdgcn_exp2f(m - mu);
             if constexpr (FSUM) l *= alpha;
