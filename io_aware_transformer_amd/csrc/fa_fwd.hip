@@ -29,13 +29,16 @@
 //    query column (lane l and l+32 share the column).  Row max and row sum are
 //    per-lane work plus one v_permlane32_swap, and the fp32 scores, once
 //    rounded to 16 bits, are already the B operand of the P.V product.
-//  * Every accumulator lives in VGPRs (about 175 per lane), so two waves
+//  * Every accumulator lives in VGPRs (about 178 per lane), so two waves
 //    share each SIMD and one issues while the other waits on LDS or on the
-//    matrix pipe.  (Measured: MFMA and VALU instructions of a SIMD do not
-//    execute at once, from one wave or two, so the softmax VALU work adds to
-//    the MFMA time; fewer VALU instructions per score is what speeds the
-//    kernel up.)  One 8-wave work-group fills a CU (128 KB of LDS); the
-//    128-key tiles halve the barriers per key against 64-key tiles.
+//    matrix pipe.  (Measured: plain VALU work of one wave overlaps the other
+//    wave's MFMAs, about 30% slower than alone, but v_dot2 instructions wait
+//    for the matrix pipe, and VALU work between one wave's own MFMAs adds to
+//    their time.  A schedule that alternates the two waves' MFMA and softmax
+//    phases kept the pipe busier but ran the power-limited chip at a lower
+//    clock and was not faster at the same accuracy.)  One 8-wave work-group
+//    fills a CU (128 KB of LDS); the 128-key tiles halve the barriers per key
+//    against 64-key tiles.
 //    Measured on MI355X and rejected: 4-wave work-groups (two per CU), a
 //    12-wave group at three waves per SIMD, an in-wave software pipeline
 //    (S(j+1) on MFMA under softmax(j)), and a V^T copy of each tile in LDS
@@ -55,8 +58,13 @@
 //  * The reference maximum m moves only when a step's maximum exceeds it by
 //    more than 8 (log2 units); then P <= 256 and the result is the same
 //    quotient, while the O rescale (64 multiplies per lane) is almost never
-//    executed.  Row reductions run as trees (v_max3) or several independent
-//    chains, never one serial dependency chain.
+//    executed.  For binary16 the reference sits a further 7 below (see
+//    kF16Lift), so tiny weights do not round to zero.  Row reductions run as
+//    trees (v_max3) or several independent chains, never one serial
+//    dependency chain.
+//  * O leaves through LDS: each wave stages its 32 rows in the idle K
+//    buffers and stores whole 16-byte row chunks, 4 (d128) or 8 (d64)
+//    complete rows per instruction.
 //
 // Causal K/V tiles wholly above the diagonal are never visited ([P-baidu]
 // §7); the last Q block of a ragged N masks keys >= N and stores no rows >= N.
@@ -64,7 +72,8 @@
 // One kernel template serves every forward entry point: MODE 0 / 1 (all
 // keys / causal: fa_fwd), 2 (sliding window and valid lengths, the mask
 // kinds of [P-baidu] §8: fa_fwd_window), 3 (one key segment per grid row,
-// merged by fa_fwd_merge_kernel: fa_fwd_split), 4 / 5 (all keys / causal
+// merged by fa_fwd_merge_kernel: fa_fwd_split, fa_fwd_split_noalloc, and
+// fa_fwd_decode, whose key sequence may be longer than the rows), 4 / 5 (all keys / causal
 // over packed variable-length sequences, the padding kind of [P-baidu] §8
 // without the padding: fa_fwd_varlen), and the DROP flag on modes 0 / 1
 // (dropout fused into the kernel, [P-wmrh] §1.2: fa_fwd_dropout).
