@@ -57,6 +57,7 @@ if str(ROOT) not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16/fp16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+PEAK_SCLK_MHZ = 2400.0        # the engine clock the published MFMA peak assumes
 TRAFFIC_FILE = ROOT / "profiles" / "fa_fwd_traffic.json"
 KERNEL_SOURCE = ROOT / "io_aware_transformer_amd" / "csrc" / "fa_fwd.hip"
 
@@ -720,6 +721,15 @@ def main() -> int:
     if clk:
         log(f"bench: engine clock under the headline load: median {clk['median']} MHz "
             f"(min {clk['min']}, max {clk['max']}, {clk['samples']} samples)")
+        # the published peak assumes 2.4 GHz; under this load the chip holds a
+        # lower clock, so the same kernel mean is also given against the MFMA
+        # peak at the measured clock (context beside roofline.frac, which
+        # stays against the published peak)
+        pk = PEAK_BF16_TFLOPS * clk["median"] / PEAK_SCLK_MHZ
+        line["clock_adjusted"] = {"sclk_mhz": clk["median"], "peak": round(pk, 1),
+                                  "unit": "TFLOP/s", "frac": round(achieved / pk, 4)}
+        log(f"bench: {100 * achieved / pk:.1f}% of the MFMA peak at {clk['median']} MHz "
+            f"({pk:.0f} TFLOP/s)")
 
     if not args.no_cold:
         tc = time_cold(w, min(args.steps, 20))
