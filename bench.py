@@ -12,7 +12,9 @@ to stderr.
                   [--backward n8k_causal_peaky] [--window n8k_causal_peaky:1023:0]
                   [--split n4k_h4_causal:4,n16k_d64:2] [--dropout n8k_causal_peaky:0.1]
                   [--varlen 32:128:8:512:8192] [--decode 1:32:1:32768,1:32:16:131072]
-                  [--spinup 0.3]
+                  [--spinup 0.3] [--last-good bench_last_good.json]
+                  [--regression-threshold 0.9] [--fail-on-regression]
+                  [--save-last-good PATH]
                   [--no-cold] [--no-cpu-baseline] [--mode copy]
 
 The headline workload is B=1 H=32 N=8192 d=128 bf16 causal with Q,K x3;
@@ -36,6 +38,13 @@ Before the warm-up steps of each record the same call runs back to back,
 untimed, for --spinup seconds (reported as spinup_s): the engine clock goes
 through a transient after idle, and the timed calls should see the clock a
 continuous load settles at.
+
+Every throughput figure of the line (the headline, each record's TFLOP/s or
+GB/s) is compared with the same figure of a stored line from the last good
+run (bench_last_good.json) and reported under "regression"; a figure below
+0.9 of its stored value is listed there, and --fail-on-regression turns that
+into exit status 4.  --save-last-good writes a run whose parity check passed
+as the new stored line.
 """
 from __future__ import annotations
 
@@ -591,13 +600,22 @@ def torch_index(rows, device):
 
 
 def cpu_model() -> str:
+    """The first processor's `model name` line of /proc/cpuinfo, with its
+    family, model and stepping numbers (virtual machines often report only a
+    generic name)."""
     try:
-        for line in Path("/proc/cpuinfo").read_text().splitlines():
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+        text = Path("/proc/cpuinfo").read_text()
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    fields = {}
+    for ln in text.splitlines():
+        if not ln.strip():
+            break                      # end of the first processor's block
+        key, _, val = ln.partition(":")
+        fields.setdefault(key.strip(), val.strip())
+    name = fields.get("model name", "unknown")
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def copy_mode(steps: int) -> None:
@@ -612,6 +630,73 @@ def copy_mode(steps: int) -> None:
     torch.cuda.synchronize()
     print(json.dumps({"mode": "copy", "bytes_read_per_launch": n * 4,
                       "bytes_written_per_launch": n * 4, "launches": steps}))
+
+
+LAST_GOOD = ROOT / "bench_last_good.json"
+REGRESSION_THRESHOLD = 0.90   # box-to-box spread of these figures is about 5-10%
+
+
+def tracked_figures(line: dict) -> dict:
+    """The throughput figures of a bench line that the regression check
+    compares (all higher-is-better), keyed by record and workload so that
+    only like is compared with like."""
+    out = {}
+
+    def put(key, v):
+        if isinstance(v, (int, float)) and not isinstance(v, bool) and v > 0:
+            out[key] = float(v)
+
+    wl = (line.get("config") or {}).get("workload", "?")
+    put(f"value[{wl}]", line.get("value"))
+    put(f"roofline.achieved[{wl}]", (line.get("roofline") or {}).get("achieved"))
+    put(f"clock_adjusted.frac[{wl}]", (line.get("clock_adjusted") or {}).get("frac"))
+    sec = line.get("secondary")
+    if sec:
+        put(f"secondary[{sec.get('workload')}].tflops", sec.get("tflops"))
+    for e in line.get("extra") or []:
+        put(f"extra[{e.get('workload')}].tflops", e.get("tflops"))
+    bw = line.get("backward")
+    if bw:
+        put(f"backward[{bw.get('workload')}].tflops", bw.get("tflops"))
+    wi = line.get("window")
+    if wi:
+        tag = f"{wi.get('workload')}:{wi.get('window_left')}:{wi.get('window_right')}"
+        put(f"window[{tag}].tflops", wi.get("tflops"))
+        put(f"window[{tag}].bwd_tflops", wi.get("bwd_tflops"))
+    for s in line.get("split") or []:
+        put(f"split[{s.get('workload')}:{s.get('num_splits')}].tflops_fa_fwd_split",
+            s.get("tflops_fa_fwd_split"))
+    for dc in line.get("decode") or []:
+        tag = f"{dc.get('B')}:{dc.get('H')}:{dc.get('Nq')}:{dc.get('Nk')}"
+        put(f"decode[{tag}].gbs", dc.get("gbs"))
+    vl = line.get("varlen")
+    if vl:
+        tag = f"{vl.get('H')}:{vl.get('d')}:{','.join(str(x) for x in vl.get('lengths', []))}"
+        put(f"varlen[{tag}].tflops", vl.get("tflops"))
+        put(f"varlen[{tag}].bwd_tflops", vl.get("bwd_tflops"))
+    dr = line.get("dropout")
+    if dr:
+        tag = f"{dr.get('workload')}:{dr.get('p_drop')}"
+        put(f"dropout[{tag}].fwd_tflops", dr.get("fwd_tflops"))
+        put(f"dropout[{tag}].bwd_tflops", dr.get("bwd_tflops"))
+    return out
+
+
+def regression_check(line: dict, good: dict | None, threshold: float,
+                     source: str = "") -> dict:
+    """Each tracked figure of `line` against the same figure of the stored
+    last good line `good`; a ratio below `threshold` is a regression."""
+    if good is None:
+        return {"last_good": source or None, "status": "missing", "ok": True}
+    cur, ref = tracked_figures(line), tracked_figures(good)
+    common = sorted(set(cur) & set(ref))
+    ratios = {k: round(cur[k] / ref[k], 4) for k in common}
+    regressed = {k: ratios[k] for k in common if ratios[k] < threshold}
+    worst = min(common, key=lambda k: ratios[k]) if common else None
+    return {"last_good": source or None, "status": "checked", "threshold": threshold,
+            "checked": len(common),
+            "worst": {"figure": worst, "ratio": ratios[worst]} if worst else None,
+            "regressed": regressed, "ok": not regressed}
 
 
 def main() -> int:
@@ -654,6 +739,16 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench")
+    ap.add_argument("--last-good", default=str(LAST_GOOD),
+                    help="stored bench line of the last good run; every tracked figure "
+                         "is compared with it under 'regression' ('none' to skip)")
+    ap.add_argument("--regression-threshold", type=float, default=REGRESSION_THRESHOLD,
+                    help="a figure below this fraction of its last good value is a "
+                         "regression")
+    ap.add_argument("--fail-on-regression", action="store_true",
+                    help="exit with status 4 when a tracked figure regressed")
+    ap.add_argument("--save-last-good", default=None, metavar="PATH",
+                    help="write this run's line to PATH when its parity check passed")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -884,7 +979,30 @@ def main() -> int:
             print(json.dumps(line), flush=True)
             log("bench: PARITY FAILED on the sampled rows; the measurement is invalid")
             return 3
+
+    regressed = False
+    if args.last_good and args.last_good != "none":
+        lg = Path(args.last_good)
+        good = json.loads(lg.read_text()) if lg.exists() else None
+        reg = regression_check(line, good, args.regression_threshold, lg.name)
+        line["regression"] = reg
+        if reg["status"] == "missing":
+            log(f"bench: no last good line at {lg}; regression check skipped")
+        else:
+            w_ = reg["worst"]
+            log(f"bench: {reg['checked']} figures against {lg.name}; worst "
+                f"{w_['figure'] if w_ else '-'} at {w_['ratio'] if w_ else '-'} of last good; "
+                + ("no regression" if reg["ok"] else f"REGRESSED: {reg['regressed']}"))
+            regressed = not reg["ok"]
     print(json.dumps(line), flush=True)
+    if args.save_last_good:
+        if args.no_cpu_baseline:
+            log("bench: --save-last-good needs the sampled parity check; not saved")
+        else:
+            Path(args.save_last_good).write_text(json.dumps(line, indent=1) + "\n")
+            log(f"bench: this line saved as the last good one at {args.save_last_good}")
+    if regressed and args.fail_on_regression:
+        return 4
     return 0
 
 

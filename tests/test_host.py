@@ -78,8 +78,8 @@ def test_bench_help_names_every_option():
     assert r.returncode == 0
     for opt in ("--gpus", "--steps", "--warmup", "--workload", "--secondary", "--extra",
                 "--backward", "--window", "--split", "--dropout", "--varlen", "--decode",
-                "--spinup",
-                "--no-cold", "--no-cpu-baseline"):
+                "--spinup", "--last-good", "--regression-threshold", "--fail-on-regression",
+                "--save-last-good", "--no-cold", "--no-cpu-baseline"):
         assert opt in r.stdout, opt
 
 
@@ -133,6 +133,40 @@ def test_bench_reads_the_marked_engine_clock(tmp_path):
     assert bench.read_sclk_mhz(str(f)) == 2400
     f.write_text("0: 500Mhz\n1: 2400Mhz\n")
     assert bench.read_sclk_mhz(str(f)) is None
+
+
+def test_bench_regression_check():
+    """Each tracked figure is compared with the same record and workload of
+    the stored line; a figure under the threshold is reported, one missing
+    from either line is not compared."""
+    import copy
+    import bench
+    good = json.loads((ROOT / "bench_last_good.json").read_text())
+    figs = bench.tracked_figures(good)
+    # the stored line is a complete default run: the headline and every record
+    for key in ("value[n8k_causal_peaky]", "roofline.achieved[n8k_causal_peaky]",
+                "secondary[n4k_causal].tflops", "extra[n16k_d64].tflops",
+                "backward[n8k_causal_peaky].tflops", "decode[1:32:1:32768].gbs"):
+        assert key in figs, key
+    assert good["config"]["workload"] == "n8k_causal_peaky"
+    assert good["parity_sample"]["floor_aware_ok"] is True
+
+    same = bench.regression_check(good, good, 0.9, "g")
+    assert same["ok"] and same["checked"] == len(figs) and same["regressed"] == {}
+    assert same["worst"]["ratio"] == 1.0
+
+    cur = copy.deepcopy(good)
+    cur["value"] = good["value"] * 0.8
+    cur["extra"][0]["tflops"] = good["extra"][0]["tflops"] * 0.95
+    cur["backward"]["workload"] = "other"       # not comparable: skipped
+    r = bench.regression_check(cur, good, 0.9, "g")
+    assert not r["ok"]
+    assert r["regressed"] == {"value[n8k_causal_peaky]": 0.8}
+    assert r["worst"] == {"figure": "value[n8k_causal_peaky]", "ratio": 0.8}
+    assert r["checked"] == len(figs) - 1
+
+    missing = bench.regression_check(good, None, 0.9, "none.json")
+    assert missing["status"] == "missing" and missing["ok"]
 
 
 def test_bench_extra_workloads_exist():
