@@ -45,3 +45,7 @@ def test_bench_json_line():
     for e in j["extra"]:
         assert e["tflops"] > 0 and abs(e["frac"] - e["tflops"] / 2500.0) < 1e-3
     assert j["parity_sample"]["floor_aware_ok"]
+    # the stored last good line is found and every default record compared
+    reg = j["regression"]
+    assert reg["status"] == "checked" and reg["last_good"] == "bench_last_good.json"
+    assert reg["checked"] >= 17 and reg["worst"]["ratio"] > 0
