@@ -2,10 +2,12 @@
 called through the C ABI) against the fp64 oracle's masked attention.
 
 Rows with keys: the forward tolerances (max abs 2e-3 fp16 / 1e-2 bf16 on o,
-1e-3 on lse), each o element also allowed its own rounding floor
-|rnd(o) - o|: a row with a window of one or two keys has weights whose
-16-bit rounding does not average out, so its error approaches two roundings.
-Rows without keys (i >= L_b): o exactly 0 and lse exactly -inf."""
+1e-3 on lse), strict first.  Each o element is also allowed its own rounding
+floor |rnd(o) - o| in two cases only: where the exact result rounded to the
+output type already misses the tolerance somewhere (as in the unmasked
+tests), and where every row sees at most two keys, whose two comparable
+weights' 16-bit rounding does not average out, so the error approaches two
+roundings.  Rows without keys (i >= L_b): o exactly 0 and lse exactly -inf."""
 from __future__ import annotations
 
 import math
@@ -55,7 +57,10 @@ def check(q, k, v, wl, wr, lens, scale):
     full = ~empty
     if full.any():
         rep = compare(o[torch.from_numpy(full)], lse[torch.from_numpy(full)], ro[full], rl[full], dt)
-        assert rep["finite"] and rep["floor_ok"], rep
+        assert rep["finite"], rep
+        if not rep["strict_ok"]:
+            two_keys = wl >= 0 and wr >= 0 and wl + wr + 1 <= 2
+            assert rep["floor_ok"] and (rep["n_floor_over_tol"] > 0 or two_keys), rep
         return rep
     return None
 
