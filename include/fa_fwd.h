@@ -181,8 +181,10 @@ fa_status fa_fwd_decode(const void *q, const void *k, const void *v, void *o,
                         int causal, float scale, int num_splits, float *ws,
                         fa_dtype dtype, hipStream_t stream);
 
-/* Bytes of ws that fa_fwd_decode needs: segments x B*H*Nq x (d + 1) fp32.
- * 0 for arguments fa_fwd_decode would reject as sizes. */
+/* Bytes of ws that fa_fwd_decode needs: segments x B*H*Nq x (d + 1) fp32,
+ * where for Nq <= 32 every key segment counts twice (two waves of its
+ * work-group each compute half of the segment's keys and leave their own
+ * partial result).  0 for arguments fa_fwd_decode would reject as sizes. */
 size_t fa_fwd_decode_workspace_size(int B, int H, int Nq, int Nk, int d,
                                     int num_splits);
 

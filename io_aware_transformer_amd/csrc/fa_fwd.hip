@@ -202,19 +202,22 @@ __device__ __forceinline__ float max2(float a, float b) {
     return r;
 }
 
-// Maximum of N values as a tree of three-input maxima (depth log3 N).
+// Maximum of N values as a tree of three-input maxima (depth log3 N): each
+// level takes the values three at a time and carries the one or two left
+// over to the next level, so N values cost ceil((N - 1) / 2) instructions.
 template <int N> struct TreeMax {
     static __device__ __forceinline__ float of(const float (&a)[N]) {
-        constexpr int M = (N + 2) / 3;
+        constexpr int T = N / 3, M = T + N % 3;
         float b[M];
 #pragma unroll
-        for (int i = 0; i < M; ++i) {
-            if (3 * i + 2 < N) b[i] = max3(a[3 * i], a[3 * i + 1], a[3 * i + 2]);
-            else if (3 * i + 1 < N) b[i] = max2(a[3 * i], a[3 * i + 1]);
-            else b[i] = a[3 * i];
-        }
+        for (int i = 0; i < T; ++i) b[i] = max3(a[3 * i], a[3 * i + 1], a[3 * i + 2]);
+#pragma unroll
+        for (int i = T; i < M; ++i) b[i] = a[3 * T + (i - T)];
         return TreeMax<M>::of(b);
     }
+};
+template <> struct TreeMax<2> {
+    static __device__ __forceinline__ float of(const float (&a)[2]) { return max2(a[0], a[1]); }
 };
 template <> struct TreeMax<1> {
     static __device__ __forceinline__ float of(const float (&a)[1]) { return a[0]; }
@@ -281,7 +284,9 @@ struct DropArgs {
 // (y = blockIdx.y) of the window rule with L_b = N; writes the segment's
 // normalised O in fp32 to PO and its lse to PL ([y][b*H+h][row]), rows
 // without keys in the segment 0 and -inf, for a merge kernel to combine.
-// Modes 0 and 1 ignore H, wl, wr, LENS, kseg, PO, PL.  4 / 5: modes 0 / 1
+// With wsplit = 2 and N <= 32 rows, waves 0 and 1 each take every other
+// 64-key step of the segment's tiles and write it as segment 2y + w.
+// Modes 0 and 1 ignore H, wl, wr, LENS, kseg, wsplit, PO, PL.  4 / 5: modes 0 / 1
 // over packed variable-length sequences: N is the token count of each head
 // ([H, N, d] tensors), LENS the cumulative sequence starts (B + 1 values),
 // BH = B*H, and work-group (b*H + h, Q block) works on sequence b of head h,
@@ -302,7 +307,7 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
                    const u16 *__restrict__ V, u16 *__restrict__ O,
                    float *__restrict__ LSE, int BH, int N_in, int nqb, float c,
                    unsigned qand, unsigned qxor, int H, int wl, int wr,
-                   const int *__restrict__ LENS, int kseg, int nk_in,
+                   const int *__restrict__ LENS, int kseg, int nk_in, int wsplit,
                    float *__restrict__ PO, float *__restrict__ PL, DropArgs dr)
 {
     static_assert(!DROP || MODE <= 1, "dropout is built for the full and causal masks");
@@ -396,7 +401,15 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(V + khead), 0, NKEYS * T::kRowBytes, kRsrcWord3);
 
-    const int q0 = qblk * kBR + kRowsPerWave * w;   // first query row of this wave
+    // Mode 3 with wsplit = 2 and at most kRowsPerWave rows (decoding shapes,
+    // where only the first wave would have rows): waves 0 and 1 both take
+    // those rows and compute alternate kBC-key steps of every LDS tile, each
+    // as a key segment of its own (partials slot 2y + w for y = blockIdx.y),
+    // so two SIMDs share the tile's compute; the other waves only load.
+    const bool dsplit = SPLIT && wsplit > 1 && N <= kRowsPerWave;
+    const bool writer = !dsplit || w < 2;           // this wave stores results
+    const int seg = dsplit ? 2 * (int)blockIdx.y + (w & 1) : (int)blockIdx.y;
+    const int q0 = qblk * kBR + kRowsPerWave * (dsplit ? 0 : w);   // first row of the wave
     const int qrow = q0 + l32;                      // the query row of this lane
 
     // Q slab -> B-operand fragments (rows past N read as zero), kept in
@@ -422,8 +435,9 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     // len: valid rows (and keys, except in mode 3, where klen = NKEYS)
     int len = N, klen = N, j_lo = 0, j_hi = -1, klo_row = 0, khi_row = -1, kbeg = 0, kend = N;
     // rows without keys: o = 0 / lse = -inf (or the fp32 partials in mode 3)
-    const size_t prow = ((size_t)blockIdx.y * BH + bh) * N + qrow;
+    const size_t prow = ((size_t)seg * BH + bh) * N + qrow;
     auto write_empty = [&]() {
+        if (!writer) return;
         if constexpr (SPLIT) {
             float *po = PO + prow * D;
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -723,6 +737,10 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         } else {
             mk = (CAUSAL && t * kBC + kBC - 1 > q0) || (t * kBC + kBC > N);
         }
+        // At d = 128 the wave index, and with it every operand of mk, is
+        // already scalar, so the flag stays on the scalar unit; at d = 64 it
+        // is made uniform explicitly.
+        if constexpr (D == 128) return mk;
         return __builtin_amdgcn_readfirstlane((int)mk) != 0;
     };
 
@@ -747,7 +765,7 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         for (int u = 0; u < kNSub; ++u) {
             const int j = kNSub * t + u;
             bool run;
-            if constexpr (GEN) run = j >= j_lo && j <= j_hi;
+            if constexpr (GEN) run = j >= j_lo && j <= j_hi && (!dsplit || u == w);
             else run = j < n_w;
             if (run) {
                 sub = u;
@@ -793,7 +811,7 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
     if constexpr (SPLIT) {
         // the segment's normalised O in fp32 and its lse; rows that met no
         // key of the segment (row sum 0) are empty
-        if (q0 < len) {
+        if (writer && q0 < len) {
             const float lht = half_sum(lh);
             const float lt = (DT == FA_DTYPE_BF16) ? half_sum(l) : lht;
             if (qrow < len) {
@@ -874,7 +892,7 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
 
 typedef void (*kernel_fn)(const u16 *, const u16 *, const u16 *, u16 *, float *,
                           int, int, int, float, unsigned, unsigned, int, int, int,
-                          const int *, int, int, float *, float *, DropArgs);
+                          const int *, int, int, int, float *, float *, DropArgs);
 
 template <int DT, int D>
 kernel_fn pick_d(int mode, bool drop)
@@ -914,44 +932,41 @@ void fa_fwd_merge_kernel(const float *__restrict__ PO, const float *__restrict__
     const long long r = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
     const int part = threadIdx.x % LPR;
     if (r >= rows) return;
+    // segments in batches of kMergeBatch: each batch's lse and O slices are
+    // requested at once, then merged into running sums kept against the
+    // largest lse seen so far (rescaled when a batch raises it)
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float sum = 0.f, mx = neg_inf();
-    if (nseg <= kMergeBatch) {
-        // every segment's lse and O slice requested at once, then combined
+    for (int s0 = 0; s0 < nseg; s0 += kMergeBatch) {
         float ls[kMergeBatch];
         f32x4 x[kMergeBatch];
 #pragma unroll
-        for (int s = 0; s < kMergeBatch; ++s) {
-            if (s < nseg) {
-                ls[s] = PL[(size_t)s * rows + r];
-                x[s] = *(const f32x4 *)(PO + ((size_t)s * rows + r) * D + 4 * part);
+        for (int i = 0; i < kMergeBatch; ++i) {
+            ls[i] = neg_inf();
+            if (s0 + i < nseg) {
+                const size_t sr = (size_t)(s0 + i) * rows + r;
+                ls[i] = PL[sr];
+                x[i] = *(const f32x4 *)(PO + sr * D + 4 * part);
             }
         }
+        float bm = mx;
 #pragma unroll
-        for (int s = 0; s < kMergeBatch; ++s)
-            if (s < nseg) mx = fmaxf(mx, ls[s]);
-        if (mx != neg_inf()) {
+        for (int i = 0; i < kMergeBatch; ++i) bm = fmaxf(bm, ls[i]);
+        if (bm == neg_inf()) continue;                // no key in any segment yet
+        if (bm != mx) {
+            const float a = (mx == neg_inf()) ? 0.f : __expf(mx - bm);
+            sum *= a;
 #pragma unroll
-            for (int s = 0; s < kMergeBatch; ++s) {
-                if (s < nseg && ls[s] != neg_inf()) {
-                    const float wgt = __expf(ls[s] - mx);
-                    sum += wgt;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, x[s][e], acc[e]);
-                }
-            }
+            for (int e = 0; e < 4; ++e) acc[e] *= a;
+            mx = bm;
         }
-    } else {
-        for (int s = 0; s < nseg; ++s) mx = fmaxf(mx, PL[(size_t)s * rows + r]);
-        if (mx != neg_inf()) {
-            for (int s = 0; s < nseg; ++s) {
-                const float ls = PL[(size_t)s * rows + r];
-                if (ls == neg_inf()) continue;
-                const float wgt = __expf(ls - mx);
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+            if (ls[i] != neg_inf()) {
+                const float wgt = __expf(ls[i] - mx);
                 sum += wgt;
-                const f32x4 x = *(const f32x4 *)(PO + ((size_t)s * rows + r) * D + 4 * part);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, x[e], acc[e]);
+                for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, x[i][e], acc[e]);
             }
         }
     }
@@ -1010,10 +1025,14 @@ fa_status launch_fwd(const void *q, const void *k, const void *v, void *o, float
                      int H, int N, int d, int mode, int wl, int wr, const int *lens,
                      float scale, fa_dtype dtype, hipStream_t stream, int nseg = 1,
                      int kseg = 0, float *po = nullptr, float *pl = nullptr,
-                     const DropArgs *drop = nullptr, int max_rows = 0, int nk = 0)
+                     const DropArgs *drop = nullptr, int max_rows = 0, int nk = 0,
+                     int wsplit = 1)
 {
     // nk > 0 (mode 3 only): the rows run against nk keys per head, and the
-    // caller has validated the differently sized tensors itself
+    // caller has validated the differently sized tensors itself.  wsplit = 2
+    // (mode 3, N <= 32 rows): two waves per work-group each compute half of
+    // every key tile as segments of their own, so po / pl hold 2 * nseg
+    // segments.
     if (mode < 4 && nk == 0) {
         const fa_status vs = validate_fwd(q, k, v, o, lse, B, H, N, d, lens, scale, dtype);
         if (vs != FA_OK) return vs;
@@ -1032,36 +1051,40 @@ fa_status launch_fwd(const void *q, const void *k, const void *v, void *o, float
     unsigned qand = (scale == 0.f) ? 0u : 0xffffffffu;
     unsigned qxor = (scale < 0.f) ? 0x80008000u : 0u;
     int bh_i = (int)BH, n_i = N, nqb_i = (int)nqb, h_i = H, wl_i = wl, wr_i = wr;
-    int kseg_i = kseg, nk_i = nk > 0 ? nk : N;
+    // the kernel splits a work-group's tiles over two waves only for mode 3
+    // problems of at most one wave's rows; the merge then sees 2 * nseg
+    const int wsp = (mode == 3 && wsplit > 1 && N <= kRowsPerWave) ? 2 : 1;
+    const long long rows = BH * N;                    // merge rows (mode 3)
+    const int rpb = 256 / (d / 4);
+    const long long g2 = (rows + rpb - 1) / rpb;
+    if (mode == 3 && g2 > INT_MAX) return FA_ERR_INVALID_ARG;
+    int kseg_i = kseg, nk_i = nk > 0 ? nk : N, wsplit_i = wsp;
     const void *qp = q, *kp = k, *vp = v;
     void *op = o;
     float *lp = lse, *pop = po, *plp = pl;
     const int *lensp = lens;
     DropArgs dr = drop ? *drop : DropArgs{0u, 0u, 0u, 256u, 1.f};
     void *args[] = {&qp, &kp, &vp, &op, &lp, &bh_i, &n_i, &nqb_i, &c, &qand, &qxor,
-                    &h_i, &wl_i, &wr_i, &lensp, &kseg_i, &nk_i, &pop, &plp, &dr};
+                    &h_i, &wl_i, &wr_i, &lensp, &kseg_i, &nk_i, &wsplit_i, &pop, &plp, &dr};
     hipError_t e = hipLaunchKernel((const void *)fn, dim3((unsigned)grid, (unsigned)nseg),
                                    dim3(kThreads), args, 0, stream);
     if (e != hipSuccess) return FA_ERR_LAUNCH;
     if (mode == 3) {
-        const long long rows = BH * N;
-        const int rpb = 256 / (d / 4);
-        const long long g2 = (rows + rpb - 1) / rpb;
-        if (g2 > INT_MAX) return FA_ERR_INVALID_ARG;
+        const int nm = nseg * wsp;                    // segments the merge combines
         if (dtype == FA_DTYPE_F16) {
             if (d == 64)
                 hipLaunchKernelGGL((fa_fwd_merge_kernel<FA_DTYPE_F16, 64>), dim3((unsigned)g2),
-                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nseg);
+                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nm);
             else
                 hipLaunchKernelGGL((fa_fwd_merge_kernel<FA_DTYPE_F16, 128>), dim3((unsigned)g2),
-                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nseg);
+                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nm);
         } else {
             if (d == 64)
                 hipLaunchKernelGGL((fa_fwd_merge_kernel<FA_DTYPE_BF16, 64>), dim3((unsigned)g2),
-                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nseg);
+                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nm);
             else
                 hipLaunchKernelGGL((fa_fwd_merge_kernel<FA_DTYPE_BF16, 128>), dim3((unsigned)g2),
-                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nseg);
+                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nm);
         }
         if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
     }
@@ -1154,6 +1177,10 @@ static int decode_splits(int B, int H, int Nq, int Nk)
     return ns < 1 ? 1 : (int)ns;
 }
 
+// Up to one wave's rows (32), two waves of each work-group compute alternate
+// halves of every key tile, each half a segment of its own.
+static int decode_wave_split(int Nq) { return Nq <= kRowsPerWave ? 2 : 1; }
+
 extern "C" int fa_fwd_decode_splits(int B, int H, int Nq, int Nk)
 {
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return 0;
@@ -1168,7 +1195,7 @@ extern "C" size_t fa_fwd_decode_workspace_size(int B, int H, int Nq, int Nk, int
         return 0;
     const int ns = num_splits ? num_splits : decode_splits(B, H, Nq, Nk);
     const int kseg = split_kseg(Nk, ns);
-    const size_t nseg = (size_t)((Nk + kseg - 1) / kseg);
+    const size_t nseg = (size_t)((Nk + kseg - 1) / kseg) * decode_wave_split(Nq);
     return nseg * (size_t)B * (size_t)H * (size_t)Nq * (size_t)(d + 1) * sizeof(float);
 }
 
@@ -1203,12 +1230,13 @@ extern "C" fa_status fa_fwd_decode(const void *q, const void *k, const void *v, 
     const int ns = num_splits ? num_splits : decode_splits(B, H, Nq, Nk);
     const int kseg = split_kseg(Nk, ns);
     const int nseg = (Nk + kseg - 1) / kseg;
+    const int wsp = decode_wave_split(Nq);
     float *po = ws;
-    float *pl = ws + (size_t)nseg * BH * Nq * d;
+    float *pl = ws + (size_t)nseg * wsp * BH * Nq * d;
     // causal: the queries are the last Nq positions, so query i may use keys
     // up to i + Nk - Nq (a window right side of Nk - Nq >= 0)
     return launch_fwd(q, k, v, o, lse, B, H, Nq, d, 3, -1, causal ? Nk - Nq : -1, nullptr,
-                      scale, dtype, stream, nseg, kseg, po, pl, nullptr, 0, Nk);
+                      scale, dtype, stream, nseg, kseg, po, pl, nullptr, 0, Nk, wsp);
 }
 
 // Split partials of fa_fwd_split_noalloc: each device holds its own copy.

@@ -261,13 +261,16 @@ def dccall(q=QD, k=KD, v=VD, o=OD, lse=LD, B=1, H=2, Nq=4, Nk=1000, d=128, causa
 
 
 def test_decode_workspace_size_and_split_rule():
-    # segments of whole 128-key tiles: Nk = 1000 in 3 splits -> 384 + 384 + 232
-    assert fa.fa_fwd_decode_workspace_size(1, 2, 4, 1000, 128, 3) == 3 * 2 * 4 * 129 * 4
-    assert fa.fa_fwd_decode_workspace_size(2, 3, 5, 100, 64, 64) == 1 * 6 * 5 * 65 * 4
+    # segments of whole 128-key tiles: Nk = 1000 in 3 splits -> 384 + 384 + 232;
+    # up to 32 query rows each segment holds two halves (two waves' partials)
+    assert fa.fa_fwd_decode_workspace_size(1, 2, 4, 1000, 128, 3) == 2 * 3 * 2 * 4 * 129 * 4
+    assert fa.fa_fwd_decode_workspace_size(2, 3, 5, 100, 64, 64) == 2 * 1 * 6 * 5 * 65 * 4
+    assert fa.fa_fwd_decode_workspace_size(1, 2, 32, 1000, 128, 3) == 2 * 3 * 2 * 32 * 129 * 4
+    assert fa.fa_fwd_decode_workspace_size(1, 2, 33, 1000, 128, 3) == 3 * 2 * 33 * 129 * 4
     # num_splits = 0 resolves to the library's rule
     ns = fa.fa_fwd_decode_splits(1, 32, 1, 32768)
     assert ns == 8      # 32 work-groups -> 8 segments of 4096 keys: 256 work-groups
-    assert fa.fa_fwd_decode_workspace_size(1, 32, 1, 32768, 128, 0) == 8 * 32 * 1 * 129 * 4
+    assert fa.fa_fwd_decode_workspace_size(1, 32, 1, 32768, 128, 0) == 2 * 8 * 32 * 1 * 129 * 4
     assert fa.fa_fwd_decode_splits(1, 1, 1, 1 << 22) == fa.FA_MAX_SPLITS
     assert fa.fa_fwd_decode_splits(1, 1, 1, 300) == 1        # under 4 tiles per segment
     assert fa.fa_fwd_decode_splits(1, 4, 300, 65536) == 32   # 8 work-groups
