@@ -57,8 +57,10 @@ def check(q, k, v, causal, scale, num_splits, dtype):
     return o, lse, rep
 
 
-@pytest.mark.parametrize("Nq,Nk", [(1, 1), (1, 129), (3, 1000), (16, 4097), (64, 300),
-                                   (100, 100), (257, 700), (300, 5000)])
+# Nq <= 32 runs two waves per key segment (each half of every key tile is a
+# segment of its own), Nq = 33 the one-wave-per-row-slab path
+@pytest.mark.parametrize("Nq,Nk", [(1, 1), (1, 129), (3, 1000), (16, 4097), (32, 1100),
+                                   (33, 1100), (64, 300), (100, 100), (257, 700), (300, 5000)])
 @pytest.mark.parametrize("splits", [0, 1, 3, 64])
 @pytest.mark.parametrize("d,dtype", [(64, "f16"), (128, "bf16")])
 @pytest.mark.parametrize("causal", [False, True])
