@@ -15,7 +15,7 @@ to stderr.
                   [--spinup 0.3] [--last-good bench_last_good.json]
                   [--regression-threshold 0.9] [--fail-on-regression]
                   [--save-last-good PATH]
-                  [--no-cold] [--no-cpu-baseline] [--mode copy]
+                  [--no-zeros] [--no-cold] [--no-cpu-baseline] [--mode copy]
 
 The headline workload is B=1 H=32 N=8192 d=128 bf16 causal with Q,K x3;
 B=2 H=16 N=4096 d=128 bf16 causal is reported beside it, the non-causal
@@ -33,6 +33,12 @@ packed sequences of seeded lengths in [512, 8192] (fa_fwd_varlen, fa_bwd_varlen,
 keys and values are read once) under "decode", and the headline forward with cold caches (a 512 MB
 buffer overwritten before each launch) under "cold".  FLOP =
 4*B*H*N^2*d, halved when causal (backward: 2.5 times that).
+
+The engine clock (pp_dpm_sclk) and board power (hwmon power1_input, with
+its cap) are sampled while the headline kernel runs back to back outside the
+timed region ("sclk_mhz", "board_power_w", "clock_adjusted"), and the same
+kernel is timed on all-zero q, k, v as a diagnostic of the clock the power
+cap allows ("zero_operands"; --no-zeros skips it).
 
 Before the warm-up steps of each record the same call runs back to back,
 untimed, for --spinup seconds (reported as spinup_s): the engine clock goes
@@ -113,13 +119,17 @@ def spin(launch, seconds: float | None = None) -> None:
         torch.cuda.synchronize()
 
 
-def time_workload(w, steps: int, warmup: int, seed: int = 0):
+def time_workload(w, steps: int, warmup: int, seed: int = 0, zeros: bool = False):
+    """HIP-event timing of fa_fwd on workload w (zeros: the same launch on
+    all-zero q, k, v, a diagnostic of the clock without data switching)."""
     import torch
     import io_aware_transformer_amd as fa
     from io_aware_transformer_amd.inputs import make_workload
 
     dev = torch.device("cuda", 0)
     q, k, v = make_workload(w, seed=seed)
+    if zeros:
+        q, k, v = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     o = torch.empty_like(qd)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
@@ -176,25 +186,36 @@ def read_sclk_mhz(path: str):
     return None
 
 
-def observed_sclk(launch, seconds: float = 1.0):
-    """Engine clock sampled every ~10 ms from a host thread while `launch`
-    keeps the GPU busy for about `seconds` (outside the timed region; the
-    clock is power-limited and depends on the load).  None where the driver
-    exposes no pp_dpm_sclk (the first card's is read)."""
+def read_power_w(path: str):
+    """Board power in watts from a hwmon power file (microwatts)."""
+    with open(path) as f:
+        return int(f.read().strip()) / 1e6
+
+
+def observed_load(launch, seconds: float = 1.0):
+    """Engine clock and board power sampled every ~10 ms from a host thread
+    while `launch` keeps the GPU busy for about `seconds` (outside the timed
+    region; under MFMA load the clock is held down by the board power cap).
+    Returns (clock, power): each a summary dict, or None where the driver
+    exposes no pp_dpm_sclk / hwmon power1_input (the first card's is read)."""
     import torch
     paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
-    if not paths:
-        return None
-    samples, stop = [], threading.Event()
+    ppaths = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input"))
+    if not paths and not ppaths:
+        return None, None
+    samples, watts, stop = [], [], threading.Event()
 
     def poll():
         while not stop.is_set():
             try:
-                mhz = read_sclk_mhz(paths[0])
-            except OSError:
+                mhz = read_sclk_mhz(paths[0]) if paths else None
+                pw = read_power_w(ppaths[0]) if ppaths else None
+            except (OSError, ValueError):
                 return
             if mhz:
                 samples.append(mhz)
+            if pw:
+                watts.append(pw)
             stop.wait(0.01)
 
     th = threading.Thread(target=poll, daemon=True)
@@ -206,11 +227,28 @@ def observed_sclk(launch, seconds: float = 1.0):
         torch.cuda.synchronize()
     stop.set()
     th.join()
-    if not samples:
-        return None
-    s = sorted(samples)
-    return {"median": s[len(s) // 2], "min": s[0], "max": s[-1], "samples": len(s),
-            "source": "pp_dpm_sclk"}
+    clock = power = None
+    if samples:
+        s = sorted(samples)
+        clock = {"median": s[len(s) // 2], "min": s[0], "max": s[-1], "samples": len(s),
+                 "source": "pp_dpm_sclk"}
+    if watts:
+        p = sorted(watts)
+        power = {"median": round(p[len(p) // 2], 1), "min": round(p[0], 1),
+                 "max": round(p[-1], 1), "samples": len(p), "cap": None,
+                 "source": "hwmon power1_input"}
+        cap = ppaths[0].replace("power1_input", "power1_cap")
+        if os.path.exists(cap):
+            try:
+                power["cap"] = round(read_power_w(cap), 1)
+            except (OSError, ValueError):
+                pass
+    return clock, power
+
+
+def observed_sclk(launch, seconds: float = 1.0):
+    """The engine clock part of observed_load."""
+    return observed_load(launch, seconds)[0]
 
 
 def time_backward(w, steps: int, warmup: int, seed: int = 0):
@@ -730,6 +768,8 @@ def main() -> int:
     ap.add_argument("--varlen", default="32:128:8:512:8192",
                     help="H:d:SEQS:MIN:MAX packed variable-length causal forward reported "
                          "beside ('none' to skip)")
+    ap.add_argument("--no-zeros", action="store_true",
+                    help="skip the all-zero-operand diagnostic of the headline kernel")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache timing of the headline workload")
     ap.add_argument("--spinup", type=float, default=SPINUP_S,
@@ -811,8 +851,12 @@ def main() -> int:
         },
     }
 
-    clk = observed_sclk(res["launch"])
+    clk, pwr = observed_load(res["launch"])
     line["sclk_mhz"] = clk
+    line["board_power_w"] = pwr
+    if pwr:
+        log(f"bench: board power under the headline load: median {pwr['median']} W "
+            f"(cap {pwr['cap']} W)")
     if clk:
         log(f"bench: engine clock under the headline load: median {clk['median']} MHz "
             f"(min {clk['min']}, max {clk['max']}, {clk['samples']} samples)")
@@ -825,6 +869,27 @@ def main() -> int:
                                   "unit": "TFLOP/s", "frac": round(achieved / pk, 4)}
         log(f"bench: {100 * achieved / pk:.1f}% of the MFMA peak at {clk['median']} MHz "
             f"({pk:.0f} TFLOP/s)")
+
+    if not args.no_zeros:
+        # diagnostic: the same kernel and launch on all-zero q, k, v.  The
+        # instructions are the same but no data switches, so the board draws
+        # less power and the clock is not held down by the power cap: this
+        # separates the schedule's cycle count from the clock the real data
+        # allows.  Never the headline.
+        rz = time_workload(w, args.steps, args.warmup, zeros=True)
+        zclk, zpwr = observed_load(rz["launch"])
+        az = w.flops / (rz["kernel_ms_mean"] * 1e-3) / 1e12
+        line["zero_operands"] = {
+            "kernel_us_mean": round(rz["kernel_ms_mean"] * 1e3, 2),
+            "tflops": round(az, 2), "frac": round(az / PEAK_BF16_TFLOPS, 4),
+            "sclk_mhz": zclk["median"] if zclk else None,
+            "board_power_w": zpwr["median"] if zpwr else None,
+            "note": "diagnostic: the headline kernel on all-zero q, k, v (same "
+                    "instructions, no data switching); not the headline"}
+        log(f"bench: {w.name} on all-zero operands: {rz['kernel_ms_mean']*1e3:.1f} us, "
+            f"{az:.1f} TFLOP/s, clock {zclk['median'] if zclk else '-'} MHz, "
+            f"power {zpwr['median'] if zpwr else '-'} W")
+        del rz
 
     if not args.no_cold:
         tc = time_cold(w, min(args.steps, 20))

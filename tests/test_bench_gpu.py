@@ -39,8 +39,10 @@ def test_bench_json_line():
     cb = j["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
     for rec in ("secondary", "backward", "window", "split", "dropout", "varlen", "decode",
-                "cold"):
+                "cold", "zero_operands", "board_power_w", "sclk_mhz"):
         assert rec in j, rec
+    z = j["zero_operands"]
+    assert z["kernel_us_mean"] > 0 and abs(z["frac"] - z["tflops"] / 2500.0) < 1e-3
     assert [e["workload"] for e in j["extra"]] == ["n4k_full", "n8k_full", "n16k_d64"]
     for e in j["extra"]:
         assert e["tflops"] > 0 and abs(e["frac"] - e["tflops"] / 2500.0) < 1e-3

@@ -79,7 +79,7 @@ def test_bench_help_names_every_option():
     for opt in ("--gpus", "--steps", "--warmup", "--workload", "--secondary", "--extra",
                 "--backward", "--window", "--split", "--dropout", "--varlen", "--decode",
                 "--spinup", "--last-good", "--regression-threshold", "--fail-on-regression",
-                "--save-last-good", "--no-cold", "--no-cpu-baseline"):
+                "--save-last-good", "--no-zeros", "--no-cold", "--no-cpu-baseline"):
         assert opt in r.stdout, opt
 
 
@@ -133,6 +133,14 @@ def test_bench_reads_the_marked_engine_clock(tmp_path):
     assert bench.read_sclk_mhz(str(f)) == 2400
     f.write_text("0: 500Mhz\n1: 2400Mhz\n")
     assert bench.read_sclk_mhz(str(f)) is None
+
+
+def test_bench_reads_board_power(tmp_path):
+    """hwmon power files hold microwatts."""
+    import bench
+    f = tmp_path / "power1_input"
+    f.write_text("1391000000\n")
+    assert bench.read_power_w(str(f)) == 1391.0
 
 
 def test_bench_regression_check():
