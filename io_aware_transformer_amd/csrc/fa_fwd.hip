@@ -467,7 +467,9 @@ void fa_fwd_kernel(const u16 *__restrict__ Q, const u16 *__restrict__ K,
         const int klo = max(wl < 0 ? 0 : max(0, r0 - wl), kbeg);
         const int khi = min(wr < 0 ? klen - 1 : min(klen - 1, r1 + wr), kend - 1);
         if (r0 > r1 || klo > khi) {                    // no (row, key) pair in the work-group
-            if (qrow < N) write_empty();
+            // (mode 3: no row of this work-group reaches the segment, and the
+            // merge reads a row's segments only up to its last allowed key)
+            if (!SPLIT && qrow < N) write_empty();
             return;
         }
         t_begin = (klo / kBC) / kNSub;
@@ -917,14 +919,17 @@ kernel_fn pick(int d, int mode, bool drop)
 // Merge of the key segments of mode 3, per row ([P-baidu] §4.2-§4.3 and the
 // split-K/V combination of "FlashAttention V2 核心原理与架构设计" §5.1):
 // lse = ln sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s, O rounded once.
-// D / 4 lanes per row, 4 elements each.
+// D / 4 lanes per row, 4 elements each.  Row i of a head (N rows) reads only
+// the segments that hold one of its keys: with a right window side wr >= 0
+// its keys end at i + wr, so segments 0 .. (i + wr) / kseg (each as wsp
+// halves); the segments past them are never read (and may be unwritten).
 constexpr int kMergeBatch = 16;   // segments whose loads the merge issues together
 
 template <int DT, int D>
 __global__ __launch_bounds__(256)
 void fa_fwd_merge_kernel(const float *__restrict__ PO, const float *__restrict__ PL,
                          u16 *__restrict__ O, float *__restrict__ LSE, long long rows,
-                         int nseg)
+                         int nseg, int N, int kseg, int wr, int wsp)
 {
     using E = Elem<DT>;
     constexpr int LPR = D / 4;
@@ -932,18 +937,24 @@ void fa_fwd_merge_kernel(const float *__restrict__ PO, const float *__restrict__
     const long long r = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
     const int part = threadIdx.x % LPR;
     if (r >= rows) return;
+    const int nm = nseg * wsp;                         // partial slots per row
+    int ns = nm;                                       // slots this row reads
+    if (wr >= 0) {
+        const long long last = (long long)(r % N) + wr;  // the row's last allowed key
+        ns = (int)min((long long)nseg, last / kseg + 1) * wsp;
+    }
     // segments in batches of kMergeBatch: each batch's lse and O slices are
     // requested at once, then merged into running sums kept against the
     // largest lse seen so far (rescaled when a batch raises it)
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float sum = 0.f, mx = neg_inf();
-    for (int s0 = 0; s0 < nseg; s0 += kMergeBatch) {
+    for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
         float ls[kMergeBatch];
         f32x4 x[kMergeBatch];
 #pragma unroll
         for (int i = 0; i < kMergeBatch; ++i) {
             ls[i] = neg_inf();
-            if (s0 + i < nseg) {
+            if (s0 + i < ns) {
                 const size_t sr = (size_t)(s0 + i) * rows + r;
                 ls[i] = PL[sr];
                 x[i] = *(const f32x4 *)(PO + sr * D + 4 * part);
@@ -1070,21 +1081,18 @@ fa_status launch_fwd(const void *q, const void *k, const void *v, void *o, float
                                    dim3(kThreads), args, 0, stream);
     if (e != hipSuccess) return FA_ERR_LAUNCH;
     if (mode == 3) {
-        const int nm = nseg * wsp;                    // segments the merge combines
+        // the merge combines nseg * wsp partial slots per row, or fewer for
+        // rows whose keys end early (wr >= 0)
+        auto merge = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3((unsigned)g2), dim3(256), 0, stream, po, pl,
+                               (u16 *)o, lse, rows, nseg, N, kseg, wr, wsp);
+        };
         if (dtype == FA_DTYPE_F16) {
-            if (d == 64)
-                hipLaunchKernelGGL((fa_fwd_merge_kernel<FA_DTYPE_F16, 64>), dim3((unsigned)g2),
-                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nm);
-            else
-                hipLaunchKernelGGL((fa_fwd_merge_kernel<FA_DTYPE_F16, 128>), dim3((unsigned)g2),
-                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nm);
+            if (d == 64) merge(fa_fwd_merge_kernel<FA_DTYPE_F16, 64>);
+            else merge(fa_fwd_merge_kernel<FA_DTYPE_F16, 128>);
         } else {
-            if (d == 64)
-                hipLaunchKernelGGL((fa_fwd_merge_kernel<FA_DTYPE_BF16, 64>), dim3((unsigned)g2),
-                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nm);
-            else
-                hipLaunchKernelGGL((fa_fwd_merge_kernel<FA_DTYPE_BF16, 128>), dim3((unsigned)g2),
-                                   dim3(256), 0, stream, po, pl, (u16 *)o, lse, rows, nm);
+            if (d == 64) merge(fa_fwd_merge_kernel<FA_DTYPE_BF16, 64>);
+            else merge(fa_fwd_merge_kernel<FA_DTYPE_BF16, 128>);
         }
         if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
     }
