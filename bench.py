@@ -37,8 +37,9 @@ buffer overwritten before each launch) under "cold".  FLOP =
 The engine clock (pp_dpm_sclk) and board power (hwmon power1_input, with
 its cap) are sampled while the headline kernel runs back to back outside the
 timed region ("sclk_mhz", "board_power_w", "clock_adjusted"), and the same
-kernel is timed on all-zero q, k, v as a diagnostic of the clock the power
-cap allows ("zero_operands"; --no-zeros skips it).
+kernel is timed on all-zero q, k, v as a diagnostic of the clock the chip
+holds without data switching in the MFMA arrays ("zero_operands"; --no-zeros
+skips it).
 
 Before the warm-up steps of each record the same call runs back to back,
 untimed, for --spinup seconds (reported as spinup_s): the engine clock goes
@@ -195,7 +196,8 @@ def read_power_w(path: str):
 def observed_load(launch, seconds: float = 1.0):
     """Engine clock and board power sampled every ~10 ms from a host thread
     while `launch` keeps the GPU busy for about `seconds` (outside the timed
-    region; under MFMA load the clock is held down by the board power cap).
+    region; under MFMA load on real data the chip's power management holds
+    the clock down).
     Returns (clock, power): each a summary dict, or None where the driver
     exposes no pp_dpm_sclk / hwmon power1_input (the first card's is read)."""
     import torch
@@ -872,10 +874,10 @@ def main() -> int:
 
     if not args.no_zeros:
         # diagnostic: the same kernel and launch on all-zero q, k, v.  The
-        # instructions are the same but no data switches, so the board draws
-        # less power and the clock is not held down by the power cap: this
-        # separates the schedule's cycle count from the clock the real data
-        # allows.  Never the headline.
+        # instructions are the same but the MFMA arrays see no data switching,
+        # and the chip then holds its full clock: this separates the
+        # schedule's cycle count from the clock that real data allows.  Never
+        # the headline.
         rz = time_workload(w, args.steps, args.warmup, zeros=True)
         zclk, zpwr = observed_load(rz["launch"])
         az = w.flops / (rz["kernel_ms_mean"] * 1e-3) / 1e12
